@@ -1,0 +1,259 @@
+"""CPU oracle of the DiLoCo outer-step merge (quantize -> fp32-domain merge -> Nesterov).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or run
+this module: only the tests, the package's smoke check and the benchmark's
+``cpu_baseline`` leg use it.  It shares no code with the HIP path.
+
+It is plain and slow on purpose: numpy, one tensor and one learner at a time,
+fp64 for every statistic, sum and optimizer step, and the fp32 formula for the
+bucket index.  Sources (the pages):
+
+  * INTELLECT-1 reading notes, "Training a 10B Model Across 3 Continents":
+      - section 3.2 (worked example): step 4 the pseudo-gradient is the start
+        weights minus the learner's end weights; step 5 mu ~ 0, sigma ~ 1.2e-3,
+        range +-7.2e-3, 256 buckets of ~5.6e-5, 64 MB -> 16 MB; step 6 the
+        learners' pseudo-gradients are averaged with the sum kept in fp32 and
+        only int8 on the wire; step 7 Nesterov outer optimizer, lr 0.7,
+        momentum 0.9.
+      - section 4.1 (uniform quantization with clipping): per-tensor mu and
+        sigma; clip to [mu - 6 sigma, mu + 6 sigma]; 256 equal buckets; each
+        codebook value is the mean of the data in its bucket, not the midpoint.
+      - section 4.2: quantization is for transport only; receivers dequantize
+        and accumulate in floating point, because Q(a) + Q(b) != Q(a + b).
+  * Decoupled DiLoCo digest, "Resilient, Distributed AI Training at Scale":
+      - section "architecture", item 4: P = 24 fragments built by greedy
+        bin-packing of whole tensors into balanced fragments (note 1);
+      - section "fault tolerance", items 1 and 3: merge once a minimum quorum
+        has arrived; learners are weighted (token/step weighted merge).
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  * sigma is the population std (ddof = 0) of the whole tensor;
+  * lo = fl32(mu - 6 sigma), hi = fl32(mu + 6 sigma), wd = fl32(12 sigma / 256);
+  * code = clip(floor(fl32(fl32(x - lo) / wd)), 0, 255), all IEEE fp32 RNE;
+  * codebook entries average the *clipped* values; an empty bucket holds its
+    midpoint fl32(lo + (c + 1/2) wd); a tensor whose wd is not a normal fp32
+    (zero variance) codes every element as 0 and every entry as fl32(mu);
+  * weights are normalised as w_i / sum_j w_j in fp64 with a left-to-right sum;
+    a zero total is a failed quorum and changes nothing;
+  * Nesterov in the PyTorch SGD form: v <- beta v + g; theta <- theta - lr (g + beta v),
+    computed in fp64 from the fp32 state and rounded back to fp32 once;
+  * greedy bin-packing = LPT: tensors by size descending (ties: lower index
+    first), each onto the least-loaded fragment (ties: lower fragment id).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+N_BUCKETS = 256
+CLIP_SIGMAS = 6.0
+FLT_MIN = float(np.finfo(np.float32).tiny)
+
+
+class NoQuorum(RuntimeError):
+    """Raised when every learner weight is zero (no learner arrived)."""
+
+
+# --- fragment plan (Decoupled DiLoCo: balanced tensor fragmentation) ---------
+
+def fragment_plan(numel, n_fragments):
+    """Greedy bin-packing of whole tensors into `n_fragments` balanced fragments.
+
+    Largest tensor first (ties: lower tensor index), each placed on the fragment
+    with the smallest load so far (ties: lower fragment id).  Returns
+    (fragment_of[T], fragment_numel[P]).
+    """
+    numel = [int(n) for n in numel]
+    loads = [0] * n_fragments
+    fragment_of = [0] * len(numel)
+    order = sorted(range(len(numel)), key=lambda t: (-numel[t], t))
+    for t in order:
+        best = 0
+        for p in range(1, n_fragments):
+            if loads[p] < loads[best]:
+                best = p
+        fragment_of[t] = best
+        loads[best] += numel[t]
+    return fragment_of, loads
+
+
+# --- stage 1: pseudo-gradient (INTELLECT-1 notes, section 3.2 step 4) ---------
+
+def pseudo_gradient(theta_global, theta_learner):
+    """Delta = theta_global - theta_learner, one IEEE fp32 subtraction per element."""
+    a = np.asarray(theta_global, dtype=np.float32)
+    b = np.asarray(theta_learner, dtype=np.float32)
+    return np.subtract(a, b, dtype=np.float32)
+
+
+# --- stage 2: per-tensor quantizer (INTELLECT-1 notes, section 4.1) -----------
+
+def tensor_stats(x):
+    """Population mean and std of one tensor's pseudo-gradient, two passes in fp64."""
+    x64 = np.asarray(x, dtype=np.float32).astype(np.float64)
+    n = x64.size
+    mu = float(np.sum(x64)) / n
+    dev = x64 - mu
+    var = float(np.sum(dev * dev)) / n
+    return mu, float(np.sqrt(var))
+
+
+def clip_range(mu, sigma):
+    """Clip range [mu - 6 sigma, mu + 6 sigma] and the width of one of 256 equal
+    buckets, each rounded once to fp32.  Returns (lo, hi, wd, mean32, degenerate)."""
+    lo = np.float32(mu - CLIP_SIGMAS * sigma)
+    hi = np.float32(mu + CLIP_SIGMAS * sigma)
+    wd = np.float32(2.0 * CLIP_SIGMAS * sigma / N_BUCKETS)
+    degenerate = not (float(wd) >= FLT_MIN)
+    return lo, hi, wd, np.float32(mu), degenerate
+
+
+def encode(x, lo, wd):
+    """Bucket index of every element: floor(fl32(fl32(x - lo) / wd)) clipped to [0, 255]."""
+    x = np.asarray(x, dtype=np.float32)
+    lo = np.float32(lo)
+    wd = np.float32(wd)
+    t = np.subtract(x, lo, dtype=np.float32)
+    q = np.divide(t, wd, dtype=np.float32)
+    c = np.clip(np.floor(q), 0.0, float(N_BUCKETS - 1))
+    return c.astype(np.uint8)
+
+
+def clip_values(x, lo, hi):
+    """The clipped pseudo-gradient min(max(x, lo), hi), fp32."""
+    return np.minimum(np.maximum(np.asarray(x, np.float32), np.float32(lo)), np.float32(hi))
+
+
+def histogram(codes, x_clipped):
+    """Per-bucket (sum of clipped values in fp64, element count)."""
+    codes = np.asarray(codes).astype(np.int64)
+    s = np.bincount(codes, weights=np.asarray(x_clipped, np.float32).astype(np.float64),
+                    minlength=N_BUCKETS)
+    n = np.bincount(codes, minlength=N_BUCKETS)
+    return s.astype(np.float64), n.astype(np.int64)
+
+
+def codebook(bucket_sum, bucket_count, lo, wd):
+    """Codebook = mean of the clipped values in each bucket, rounded once to fp32;
+    an empty bucket holds its midpoint."""
+    cb = np.empty(N_BUCKETS, dtype=np.float32)
+    for c in range(N_BUCKETS):
+        if bucket_count[c] > 0:
+            cb[c] = np.float32(bucket_sum[c] / float(bucket_count[c]))
+        else:
+            cb[c] = np.float32(float(lo) + (c + 0.5) * float(wd))
+    return cb
+
+
+def quantize_tensor(x, given_range=None):
+    """Quantize one learner's pseudo-gradient of one tensor.
+
+    Returns a dict with mu, sigma, lo, hi, wd, mean32, degenerate, codes,
+    bucket_sum, bucket_count and codebook.  `given_range` = (lo, hi, wd, mean32)
+    skips the statistics and uses that range instead.
+    """
+    x = np.asarray(x, dtype=np.float32).ravel()
+    if given_range is None:
+        mu, sigma = tensor_stats(x)
+        lo, hi, wd, m32, degenerate = clip_range(mu, sigma)
+    else:
+        lo, hi, wd, m32 = (np.float32(v) for v in given_range)
+        mu, sigma = float(m32), float("nan")
+        degenerate = not (float(wd) >= FLT_MIN)
+    if degenerate:
+        codes = np.zeros(x.size, dtype=np.uint8)
+        s, n = histogram(codes, clip_values(x, lo, hi))
+        cb = np.full(N_BUCKETS, m32, dtype=np.float32)
+    else:
+        codes = encode(x, lo, wd)
+        s, n = histogram(codes, clip_values(x, lo, hi))
+        cb = codebook(s, n, lo, wd)
+    return dict(mu=mu, sigma=sigma, lo=lo, hi=hi, wd=wd, mean32=m32,
+                degenerate=degenerate, codes=codes, bucket_sum=s, bucket_count=n,
+                codebook=cb)
+
+
+def dequantize(codes, cb):
+    """fp32 value of every code under its codebook."""
+    return np.asarray(cb, np.float32)[np.asarray(codes).astype(np.int64)]
+
+
+# --- stage 3: weighted merge in the float domain (sections 3.2 step 6, 4.2) ---
+
+def normalize_weights(weights):
+    """w_i / sum_j w_j in fp64 (left-to-right sum).  Zero total -> NoQuorum."""
+    w = [float(v) for v in weights]
+    if any(not (v >= 0.0) for v in w):
+        raise ValueError("weights must be >= 0")
+    total = 0.0
+    for v in w:
+        total += v
+    if not (total > 0.0):
+        raise NoQuorum("no learner present")
+    return [v / total for v in w]
+
+
+def merge(codes_per_learner, codebook_per_learner, w_hat):
+    """g = sum_i w_hat_i * cb_i[code_i] in fp64, learners in index order; a learner
+    with weight 0 is skipped (never read)."""
+    g = None
+    for codes, cb, w in zip(codes_per_learner, codebook_per_learner, w_hat):
+        if w == 0.0:
+            continue
+        term = np.float64(w) * dequantize(codes, cb).astype(np.float64)
+        g = term if g is None else g + term
+    return g
+
+
+# --- stage 4: Nesterov outer step (section 3.2 step 7) ------------------------
+
+def nesterov(theta, momentum, g, lr=0.7, beta=0.9):
+    """PyTorch SGD-Nesterov form, dampening 0: v <- beta v + g;
+    theta <- theta - lr (g + beta v).  fp64 arithmetic, fp32 state out."""
+    th = np.asarray(theta, np.float32).astype(np.float64)
+    v = np.asarray(momentum, np.float32).astype(np.float64)
+    g = np.asarray(g, np.float64)
+    v_new = beta * v + g
+    th_new = th - lr * (g + beta * v_new)
+    return th_new.astype(np.float32), v_new.astype(np.float32)
+
+
+# --- one merge call over a fragment -------------------------------------------
+
+def outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights,
+               present=None, lr=0.7, beta=0.9, given_ranges=None):
+    """One outer step over the tensors of one fragment.
+
+    theta_g, momentum : fp32 flat arrays (not modified; new copies are returned)
+    theta_L           : fp32 [K, learner_stride]
+    tensors           : list of (offset, loffset, numel)
+    weights           : raw learner weights; 0 = absent
+    present           : learners that quantize (default: weight > 0)
+    given_ranges      : optional {(i, t): (lo, hi, wd, mean32)} pinned ranges
+
+    Returns dict(theta=..., momentum=..., quant={(i, t): quantize_tensor dict},
+    g={t: fp64 merged pseudo-gradient}).  Raises NoQuorum when all weights are 0.
+    """
+    k = theta_L.shape[0]
+    w_hat = normalize_weights(weights)
+    if present is None:
+        present = [1 if w > 0 else 0 for w in weights]
+    th = np.array(theta_g, dtype=np.float32, copy=True)
+    mom = np.array(momentum, dtype=np.float32, copy=True)
+    quant, gs = {}, {}
+    for t, (off, loff, n) in enumerate(tensors):
+        tg = th[off:off + n]
+        codes, cbs, ws = [], [], []
+        for i in range(k):
+            if not present[i]:
+                continue
+            x = pseudo_gradient(tg, theta_L[i, loff:loff + n])
+            gr = None if given_ranges is None else given_ranges.get((i, t))
+            q = quantize_tensor(x, gr)
+            quant[(i, t)] = q
+            codes.append(q["codes"])
+            cbs.append(q["codebook"])
+            ws.append(w_hat[i])
+        g = merge(codes, cbs, ws)
+        gs[t] = g
+        th[off:off + n], mom[off:off + n] = nesterov(tg, mom[off:off + n], g, lr, beta)
+    return dict(theta=th, momentum=mom, quant=quant, g=gs)

@@ -1,0 +1,109 @@
+"""Planted mistakes in the CPU oracle must each fail at least one pin.
+
+Each case swaps one oracle function (or constant) for a plausible wrong version,
+runs the pins that should notice, and expects an AssertionError.  Everything
+runs on the CPU; the real oracle is restored after each case.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import oracle.core as core
+from tests import test_oracle_pins as pins
+
+
+def _patch(monkeypatch, name, value):
+    monkeypatch.setattr(core, name, value)
+    if hasattr(oracle, name):
+        monkeypatch.setattr(oracle, name, value)
+
+
+def _sample_std(x):
+    x64 = np.asarray(x, np.float32).astype(np.float64)
+    mu = float(np.mean(x64))
+    return mu, float(np.sqrt(np.sum((x64 - mu) ** 2) / (x64.size - 1)))
+
+
+def _midpoint_codebook(s, n, lo, wd):
+    return np.array([np.float32(float(lo) + (c + 0.5) * float(wd)) for c in range(256)], np.float32)
+
+
+def _wrong_sign(a, b):
+    return np.subtract(np.asarray(b, np.float32), np.asarray(a, np.float32), dtype=np.float32)
+
+
+def _unnormalized(w):
+    return [float(v) for v in w]
+
+
+def _heavy_ball(theta, momentum, g, lr=0.7, beta=0.9):
+    th = np.asarray(theta, np.float32).astype(np.float64)
+    v = beta * np.asarray(momentum, np.float32).astype(np.float64) + np.asarray(g, np.float64)
+    return (th - lr * v).astype(np.float32), v.astype(np.float32)
+
+
+def _round_not_floor(x, lo, wd):
+    t = np.subtract(np.asarray(x, np.float32), np.float32(lo), dtype=np.float32)
+    q = np.divide(t, np.float32(wd), dtype=np.float32)
+    return np.clip(np.rint(q), 0, 255).astype(np.uint8)
+
+
+def _lpt_last_tie(numel, n_fragments):
+    loads = [0] * n_fragments
+    frag = [0] * len(numel)
+    for t in sorted(range(len(numel)), key=lambda t: (-numel[t], t)):
+        best = max(range(n_fragments), key=lambda p: (-loads[p], p))
+        frag[t] = best
+        loads[best] += numel[t]
+    return frag, loads
+
+
+MUTATIONS = {
+    "clip_at_5_sigma": (lambda mp: _patch(mp, "CLIP_SIGMAS", 5.0),
+                        [pins.test_worked_example_range_from_printed_sigma]),
+    "sample_std": (lambda mp: _patch(mp, "tensor_stats", _sample_std),
+                   [pins.test_stats_arithmetic_progression]),
+    "midpoint_codebook": (lambda mp: _patch(mp, "codebook", _midpoint_codebook),
+                          [lambda: pins.test_histogram_and_codebook_bruteforce(0)]),
+    "pseudo_gradient_sign": (lambda mp: _patch(mp, "pseudo_gradient", _wrong_sign),
+                             [pins.test_fedavg_reduction_pins_the_sign]),
+    "weights_not_normalized": (lambda mp: _patch(mp, "normalize_weights", _unnormalized),
+                               [pins.test_merge_identical_learners]),
+    "heavy_ball_not_nesterov": (lambda mp: _patch(mp, "nesterov", _heavy_ball),
+                                [pins.test_nesterov_closed_form_constant_g,
+                                 pins.test_nesterov_matches_torch_sgd]),
+    "round_not_floor": (lambda mp: _patch(mp, "encode", _round_not_floor),
+                        [pins.test_encode_exact_grid_boundaries]),
+    "lpt_ties_to_last_fragment": (lambda mp: _patch(mp, "fragment_plan", _lpt_last_tie),
+                                  [pins.test_lpt_hand_worked]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(monkeypatch, name):
+    apply, checks = MUTATIONS[name]
+    apply(monkeypatch)
+    for check in checks:
+        with pytest.raises(AssertionError):
+            check()
+
+
+def test_width_over_255_is_caught(monkeypatch):
+    orig = core.clip_range
+
+    def width_255(mu, sigma):
+        lo, hi, _, m, deg = orig(mu, sigma)
+        return lo, hi, np.float32(12 * sigma / 255), m, deg
+
+    _patch(monkeypatch, "clip_range", width_255)
+    with pytest.raises(AssertionError):
+        pins.test_worked_example_4096x4096()
+
+
+def test_unclipped_codebook_is_caught(monkeypatch):
+    """Averaging raw instead of clipped values moves the edge entries outside the range."""
+    orig = core.clip_values
+    _patch(monkeypatch, "clip_values", lambda x, lo, hi: np.asarray(x, np.float32))
+    with pytest.raises(AssertionError):
+        pins.test_histogram_and_codebook_bruteforce(0)
+    _patch(monkeypatch, "clip_values", orig)
