@@ -1,0 +1,198 @@
+"""DiLoCo outer-step merge on one MI355X (gfx950): Python binding of libdlc.so.
+
+The functions here carry the C ABI's names (include/dlc.h) and only marshal
+arguments: torch tensors supply device memory, torch's current HIP stream is the
+default stream, and every step of the computation runs in the library's kernels.
+Importing this package fails loudly if the library has not been built
+(``python -m diloco_outer_step_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdlc.so")
+
+DLC_OK = 0
+DLC_ERR_INVALID_ARGUMENT = -1
+DLC_ERR_ALIGNMENT = -2
+DLC_ERR_NO_QUORUM = -3
+DLC_ERR_WORKSPACE = -4
+DLC_ERR_HIP = -5
+DLC_RANGE_GIVEN = 1
+DLC_MAX_LEARNERS = 64
+DLC_N_BUCKETS = 256
+DLC_ALIGN_ELEMS = 64
+DLC_RANGE_FIELDS = 4
+
+EXPORTED = (
+    "dlc_fragment_plan", "dlc_workspace_bytes", "dlc_quantize_range", "dlc_quantize_encode",
+    "dlc_quantize", "dlc_merge_outer_step", "dlc_last_error", "dlc_version",
+)
+
+
+class DlcError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"dlc error {code}: {message}")
+        self.code = code
+
+
+class NoQuorumError(DlcError):
+    pass
+
+
+class _Tensor(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("loffset", ctypes.c_int64), ("numel", ctypes.c_int64)]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m diloco_outer_step_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
+    tp = ctypes.POINTER(_Tensor)
+    sig = {
+        "dlc_fragment_plan": [vp, i32, i32, vp, vp],
+        "dlc_workspace_bytes": [i32, tp, i32, ctypes.POINTER(sz)],
+        "dlc_quantize_range": [vp, vp, i64, i32, vp, tp, i32, vp, vp, sz, vp],
+        "dlc_quantize_encode": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, vp, sz, vp],
+        "dlc_quantize": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, u32, vp, sz, vp],
+        "dlc_merge_outer_step": [vp, vp, vp, i64, i32, vp, vp, tp, i32, ctypes.c_double,
+                                 ctypes.c_double, u32, vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = i32
+    for name in ("dlc_last_error", "dlc_version"):
+        fn = getattr(lib, name)
+        fn.argtypes = []
+        fn.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def _check(rc: int) -> None:
+    if rc != DLC_OK:
+        msg = _lib.dlc_last_error().decode()
+        if rc == DLC_ERR_NO_QUORUM:
+            raise NoQuorumError(rc, msg)
+        raise DlcError(rc, msg)
+
+
+def _tensors(tensors: Sequence[Tuple[int, int, int]]):
+    arr = (_Tensor * max(1, len(tensors)))()
+    for i, (o, lo, n) in enumerate(tensors):
+        arr[i].offset, arr[i].loffset, arr[i].numel = int(o), int(lo), int(n)
+    return arr, len(tensors)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _present(present, k):
+    if present is None:
+        return None, None
+    buf = (ctypes.c_uint8 * k)(*[1 if p else 0 for p in present])
+    return buf, ctypes.cast(buf, ctypes.c_void_p)
+
+
+def _learner_stride(theta_L: torch.Tensor) -> int:
+    if theta_L.dim() != 2 or not theta_L.is_contiguous():
+        raise ValueError("theta_L must be a contiguous [K, learner_stride] tensor")
+    return theta_L.shape[1]
+
+
+def dlc_version() -> str:
+    return _lib.dlc_version().decode()
+
+
+def dlc_last_error() -> str:
+    return _lib.dlc_last_error().decode()
+
+
+def dlc_fragment_plan(numel: Sequence[int], n_fragments: int):
+    """Greedy bin-packing of whole tensors -> (fragment_of list, fragment_numel list)."""
+    n = len(numel)
+    src = (ctypes.c_int64 * max(1, n))(*[int(v) for v in numel])
+    frag = (ctypes.c_int32 * max(1, n))()
+    loads = (ctypes.c_int64 * max(1, n_fragments))()
+    _check(_lib.dlc_fragment_plan(ctypes.cast(src, ctypes.c_void_p), n, int(n_fragments),
+                                  ctypes.cast(frag, ctypes.c_void_p), ctypes.cast(loads, ctypes.c_void_p)))
+    return list(frag[:n]), list(loads[:n_fragments])
+
+
+def dlc_workspace_bytes(n_learners: int, tensors) -> int:
+    arr, n = _tensors(tensors)
+    out = ctypes.c_size_t(0)
+    _check(_lib.dlc_workspace_bytes(int(n_learners), arr, n, ctypes.byref(out)))
+    return out.value
+
+
+def alloc_workspace(n_learners: int, tensors, device="cuda") -> torch.Tensor:
+    nbytes = max(256, dlc_workspace_bytes(n_learners, tensors))
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def dlc_quantize_range(theta_g, theta_L, tensors, range_out, workspace, present=None, stream=None):
+    k = theta_L.shape[0]
+    arr, n = _tensors(tensors)
+    _buf, pres = _present(present, k)
+    _check(_lib.dlc_quantize_range(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, pres, arr, n,
+                                   _ptr(range_out), _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dlc_quantize_encode(theta_g, theta_L, tensors, range_in, codes, codebook, workspace, present=None,
+                        stream=None):
+    k = theta_L.shape[0]
+    arr, n = _tensors(tensors)
+    _buf, pres = _present(present, k)
+    _check(_lib.dlc_quantize_encode(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, pres, arr, n,
+                                    _ptr(range_in), _ptr(codes), _ptr(codebook), _ptr(workspace),
+                                    workspace.numel(), _stream(stream)))
+
+
+def dlc_quantize(theta_g, theta_L, tensors, codes, codebook, range_io, workspace, present=None,
+                 range_given=False, stream=None):
+    k = theta_L.shape[0]
+    arr, n = _tensors(tensors)
+    _buf, pres = _present(present, k)
+    flags = DLC_RANGE_GIVEN if range_given else 0
+    _check(_lib.dlc_quantize(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, pres, arr, n,
+                             _ptr(codes), _ptr(codebook), _ptr(range_io), flags, _ptr(workspace),
+                             workspace.numel(), _stream(stream)))
+
+
+def dlc_merge_outer_step(theta_g, momentum, codes, codebook, weights, tensors, lr=0.7, beta=0.9,
+                         stream=None):
+    k = codes.shape[0]
+    if codes.dim() != 2 or not codes.is_contiguous():
+        raise ValueError("codes must be a contiguous [K, learner_stride] uint8 tensor")
+    w = (ctypes.c_double * k)(*[float(x) for x in weights])
+    arr, n = _tensors(tensors)
+    _check(_lib.dlc_merge_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(codes), codes.shape[1], k,
+                                     _ptr(codebook), ctypes.cast(w, ctypes.c_void_p), arr, n, float(lr),
+                                     float(beta), 0, _stream(stream)))
+
+
+def outputs_for(n_learners: int, learner_stride: int, n_tensors: int, device="cuda"):
+    """Allocate (codes, codebook, range) buffers for a call."""
+    codes = torch.empty((n_learners, learner_stride), dtype=torch.uint8, device=device)
+    codebook = torch.empty((n_learners, n_tensors, DLC_N_BUCKETS), dtype=torch.float32, device=device)
+    rng = torch.empty((n_learners, n_tensors, DLC_RANGE_FIELDS), dtype=torch.float32, device=device)
+    return codes, codebook, rng

@@ -1,0 +1,344 @@
+// C ABI of the DiLoCo outer-step merge: argument checks, the fragment planner,
+// the block partition of a call, and kernel launch orchestration.
+//
+// Nothing here allocates device memory, keeps state between calls or waits on the
+// stream; argument errors are reported before anything is enqueued.
+#include "dlc.h"
+#include "dlc_internal.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int32_t fail(int32_t code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int32_t ok() {
+  g_last_error.clear();
+  return DLC_OK;
+}
+
+// Target number of blocks per streaming launch: a few resident blocks per CU on
+// a 256-CU part, so that the tensor-aligned partition stays balanced.
+constexpr int64_t kTargetBlocks = 2048;
+
+bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
+
+struct Partition {
+  std::vector<dlc::LaunchGeom> launches;
+  int64_t n_slots = 0;
+};
+
+// Split the call's tensors into launches of at most kMaxTensorsPerLaunch tensors;
+// each tensor gets ceil(tiles / tiles_per_block) blocks, tiles_per_block chosen
+// from the whole call so that the call has about kTargetBlocks blocks.
+Partition make_partition(const dlc_tensor* t, int32_t n) {
+  Partition p;
+  int64_t total_tiles = 0;
+  for (int32_t i = 0; i < n; ++i) total_tiles += (t[i].numel + dlc::kTile - 1) / dlc::kTile;
+  const int64_t tpb = std::max<int64_t>(1, (total_tiles + kTargetBlocks - 1) / kTargetBlocks);
+  for (int32_t s = 0; s < n; s += dlc::kMaxTensorsPerLaunch) {
+    dlc::LaunchGeom g;
+    std::memset(&g, 0, sizeof(g));
+    g.n_tensors = std::min<int32_t>(dlc::kMaxTensorsPerLaunch, n - s);
+    g.t_base = s;
+    g.n_tensors_call = n;
+    g.tiles_per_block = (int32_t)tpb;
+    g.slot_base = (int32_t)p.n_slots;
+    int64_t blocks = 0;
+    for (int32_t i = 0; i < g.n_tensors; ++i) {
+      const dlc_tensor& d = t[s + i];
+      g.t[i].offset = d.offset;
+      g.t[i].loffset = d.loffset;
+      g.t[i].numel = d.numel;
+      g.t[i].block_first = (int32_t)blocks;
+      const int64_t tiles = (d.numel + dlc::kTile - 1) / dlc::kTile;
+      blocks += (tiles + tpb - 1) / tpb;
+    }
+    g.n_blocks = (int32_t)blocks;
+    p.n_slots += blocks;
+    p.launches.push_back(g);
+  }
+  return p;
+}
+
+struct WorkspaceLayout {
+  size_t stats = 0, sum = 0, cnt = 0, total = 0;
+};
+
+size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
+
+WorkspaceLayout workspace_layout(int64_t n_slots, int32_t n_learners) {
+  WorkspaceLayout w;
+  const size_t per = (size_t)n_slots * (size_t)n_learners;
+  w.stats = 0;
+  w.sum = round256(per * sizeof(double) * 2);
+  w.cnt = w.sum + round256(per * dlc::kBuckets * sizeof(double));
+  w.total = w.cnt + round256(per * dlc::kBuckets * sizeof(uint32_t));
+  return w;
+}
+
+int32_t check_tensors(const dlc_tensor* t, int32_t n, int64_t learner_stride, bool need_loffset) {
+  if (t == nullptr) return fail(DLC_ERR_INVALID_ARGUMENT, "tensors is NULL");
+  if (n < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "n_tensors must be >= 1");
+  if (need_loffset && (learner_stride < 1 || learner_stride % DLC_ALIGN_ELEMS != 0))
+    return fail(DLC_ERR_ALIGNMENT, "learner_stride must be a positive multiple of 64 elements");
+  for (int32_t i = 0; i < n; ++i) {
+    const dlc_tensor& d = t[i];
+    if (d.numel < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "tensor " + std::to_string(i) + ": numel must be >= 1");
+    if (d.offset < 0 || d.loffset < 0)
+      return fail(DLC_ERR_INVALID_ARGUMENT, "tensor " + std::to_string(i) + ": negative offset");
+    if (d.offset % DLC_ALIGN_ELEMS != 0 || d.loffset % DLC_ALIGN_ELEMS != 0)
+      return fail(DLC_ERR_ALIGNMENT, "tensor " + std::to_string(i) + ": offset and loffset must be multiples of 64 elements");
+    if (need_loffset && d.loffset + d.numel > learner_stride)
+      return fail(DLC_ERR_INVALID_ARGUMENT, "tensor " + std::to_string(i) + ": loffset + numel exceeds learner_stride");
+  }
+  // No two tensors may overlap in theta_global, nor within a learner row.
+  std::vector<int32_t> order(n);
+  for (int pass = 0; pass < 2; ++pass) {
+    std::iota(order.begin(), order.end(), 0);
+    auto key = [&](int32_t i) { return pass == 0 ? t[i].offset : t[i].loffset; };
+    std::sort(order.begin(), order.end(), [&](int32_t x, int32_t y) { return key(x) < key(y); });
+    for (int32_t i = 1; i < n; ++i) {
+      if (key(order[i - 1]) + t[order[i - 1]].numel > key(order[i]))
+        return fail(DLC_ERR_INVALID_ARGUMENT, std::string("tensors ") + std::to_string(order[i - 1]) + " and " +
+                                                  std::to_string(order[i]) + " overlap in " +
+                                                  (pass == 0 ? "theta_global" : "the learner rows"));
+    }
+  }
+  return DLC_OK;
+}
+
+struct Common {
+  dlc::QuantArgs args;
+  Partition part;
+  hipStream_t stream;
+};
+
+// Shared checks and setup of the quantize stages.
+int32_t setup_quant(Common& c, const float* theta_global, const float* theta_learners,
+                    int64_t learner_stride, int32_t n_learners, const uint8_t* present,
+                    const dlc_tensor* tensors, int32_t n_tensors, void* workspace,
+                    size_t workspace_bytes, void* hip_stream) {
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  if (!theta_global || !theta_learners) return fail(DLC_ERR_INVALID_ARGUMENT, "theta pointer is NULL");
+  if (!aligned256(theta_global) || !aligned256(theta_learners))
+    return fail(DLC_ERR_ALIGNMENT, "theta pointers must be 256-byte aligned");
+  int32_t rc = check_tensors(tensors, n_tensors, learner_stride, true);
+  if (rc != DLC_OK) return rc;
+  std::memset(&c.args, 0, sizeof(c.args));
+  int32_t kp = 0;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (present == nullptr || present[i] != 0) c.args.learner[kp++] = i;
+  }
+  if (kp == 0) return fail(DLC_ERR_NO_QUORUM, "no learner is present");
+  c.part = make_partition(tensors, n_tensors);
+  const WorkspaceLayout wl = workspace_layout(c.part.n_slots, kp);
+  if (workspace == nullptr || workspace_bytes < wl.total)
+    return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(wl.total) + " bytes");
+  if (!aligned256(workspace)) return fail(DLC_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  c.args.theta_g = theta_global;
+  c.args.theta_L = theta_learners;
+  c.args.stride = learner_stride;
+  c.args.n_present = kp;
+  c.args.part_stats = reinterpret_cast<double2*>(ws + wl.stats);
+  c.args.part_sum = reinterpret_cast<double*>(ws + wl.sum);
+  c.args.part_cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
+  c.stream = static_cast<hipStream_t>(hip_stream);
+  return DLC_OK;
+}
+
+int32_t hip_fail(hipError_t e, const char* what) {
+  return fail(DLC_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int32_t run_range(Common& c) {
+  for (const dlc::LaunchGeom& g : c.part.launches) {
+    for (int32_t k0 = 0; k0 < c.args.n_present; k0 += dlc::kLearnerChunk) {
+      c.args.k_base = k0;
+      c.args.k_count = std::min(dlc::kLearnerChunk, c.args.n_present - k0);
+      hipError_t e = dlc::launch_stats(c.args, g, c.stream);
+      if (e != hipSuccess) return hip_fail(e, "stats kernel launch");
+    }
+    hipError_t e = dlc::launch_range(c.args, g, c.stream);
+    if (e != hipSuccess) return hip_fail(e, "range kernel launch");
+  }
+  return DLC_OK;
+}
+
+int32_t run_encode(Common& c) {
+  for (const dlc::LaunchGeom& g : c.part.launches) {
+    for (int32_t k0 = 0; k0 < c.args.n_present; k0 += dlc::kLearnerChunk) {
+      c.args.k_base = k0;
+      c.args.k_count = std::min(dlc::kLearnerChunk, c.args.n_present - k0);
+      hipError_t e = dlc::launch_encode(c.args, g, c.stream);
+      if (e != hipSuccess) return hip_fail(e, "encode kernel launch");
+    }
+    hipError_t e = dlc::launch_codebook(c.args, g, c.stream);
+    if (e != hipSuccess) return hip_fail(e, "codebook kernel launch");
+  }
+  return DLC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t dlc_fragment_plan(const int64_t* numel, int32_t n_tensors, int32_t n_fragments,
+                          int32_t* fragment_of, int64_t* fragment_numel) {
+  if (!numel || !fragment_of) return fail(DLC_ERR_INVALID_ARGUMENT, "numel and fragment_of must not be NULL");
+  if (n_tensors < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "n_tensors must be >= 1");
+  if (n_fragments < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "n_fragments must be >= 1");
+  for (int32_t i = 0; i < n_tensors; ++i)
+    if (numel[i] < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "numel must be >= 1");
+  std::vector<int32_t> order(n_tensors);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return numel[a] > numel[b]; });
+  std::vector<int64_t> load(n_fragments, 0);
+  for (int32_t t : order) {
+    int32_t best = 0;
+    for (int32_t p = 1; p < n_fragments; ++p)
+      if (load[p] < load[best]) best = p;
+    fragment_of[t] = best;
+    load[best] += numel[t];
+  }
+  if (fragment_numel) std::copy(load.begin(), load.end(), fragment_numel);
+  return ok();
+}
+
+int32_t dlc_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                            size_t* bytes) {
+  if (!bytes) return fail(DLC_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  int32_t rc = check_tensors(tensors, n_tensors, 0, false);
+  if (rc != DLC_OK) return rc;
+  const Partition p = make_partition(tensors, n_tensors);
+  *bytes = workspace_layout(p.n_slots, n_learners).total;
+  return ok();
+}
+
+int32_t dlc_quantize_range(const float* theta_global, const float* theta_learners,
+                           int64_t learner_stride, int32_t n_learners, const uint8_t* present,
+                           const dlc_tensor* tensors, int32_t n_tensors, float* range,
+                           void* workspace, size_t workspace_bytes, void* hip_stream) {
+  Common c;
+  int32_t rc = setup_quant(c, theta_global, theta_learners, learner_stride, n_learners, present, tensors,
+                           n_tensors, workspace, workspace_bytes, hip_stream);
+  if (rc != DLC_OK) return rc;
+  if (!range) return fail(DLC_ERR_INVALID_ARGUMENT, "range is NULL");
+  if (!aligned256(range)) return fail(DLC_ERR_ALIGNMENT, "range must be 256-byte aligned");
+  c.args.range = reinterpret_cast<float4*>(range);
+  rc = run_range(c);
+  return rc == DLC_OK ? ok() : rc;
+}
+
+int32_t dlc_quantize_encode(const float* theta_global, const float* theta_learners,
+                            int64_t learner_stride, int32_t n_learners, const uint8_t* present,
+                            const dlc_tensor* tensors, int32_t n_tensors, const float* range,
+                            uint8_t* codes, float* codebook, void* workspace,
+                            size_t workspace_bytes, void* hip_stream) {
+  Common c;
+  int32_t rc = setup_quant(c, theta_global, theta_learners, learner_stride, n_learners, present, tensors,
+                           n_tensors, workspace, workspace_bytes, hip_stream);
+  if (rc != DLC_OK) return rc;
+  if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
+  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
+    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
+  c.args.range = reinterpret_cast<float4*>(const_cast<float*>(range));
+  c.args.codes = codes;
+  c.args.codebook = codebook;
+  rc = run_encode(c);
+  return rc == DLC_OK ? ok() : rc;
+}
+
+int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
+                     int64_t learner_stride, int32_t n_learners, const uint8_t* present,
+                     const dlc_tensor* tensors, int32_t n_tensors, uint8_t* codes,
+                     float* codebook, float* range, uint32_t flags, void* workspace,
+                     size_t workspace_bytes, void* hip_stream) {
+  if ((flags & ~DLC_RANGE_GIVEN) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
+  Common c;
+  int32_t rc = setup_quant(c, theta_global, theta_learners, learner_stride, n_learners, present, tensors,
+                           n_tensors, workspace, workspace_bytes, hip_stream);
+  if (rc != DLC_OK) return rc;
+  if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
+  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
+    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
+  c.args.range = reinterpret_cast<float4*>(range);
+  c.args.codes = codes;
+  c.args.codebook = codebook;
+  if ((flags & DLC_RANGE_GIVEN) == 0) {
+    rc = run_range(c);
+    if (rc != DLC_OK) return rc;
+  }
+  rc = run_encode(c);
+  return rc == DLC_OK ? ok() : rc;
+}
+
+int32_t dlc_merge_outer_step(float* theta_global, float* momentum, const uint8_t* codes,
+                             int64_t learner_stride, int32_t n_learners, const float* codebook,
+                             const double* weights, const dlc_tensor* tensors, int32_t n_tensors,
+                             double lr, double beta, uint32_t flags, void* hip_stream) {
+  if (flags != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "flags must be 0");
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  if (!theta_global || !momentum || !codes || !codebook || !weights)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "theta_global, momentum, codes, codebook and weights must not be NULL");
+  if (!aligned256(theta_global) || !aligned256(momentum) || !aligned256(codes) || !aligned256(codebook))
+    return fail(DLC_ERR_ALIGNMENT, "device pointers must be 256-byte aligned");
+  if (!std::isfinite(lr) || !std::isfinite(beta)) return fail(DLC_ERR_INVALID_ARGUMENT, "lr and beta must be finite");
+  int32_t rc = check_tensors(tensors, n_tensors, learner_stride, true);
+  if (rc != DLC_OK) return rc;
+  // Normalize in fp64 with a left-to-right sum over all learners.
+  double total = 0.0;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (!(weights[i] >= 0.0) || !std::isfinite(weights[i]))
+      return fail(DLC_ERR_INVALID_ARGUMENT, "weights must be finite and >= 0");
+    total += weights[i];
+  }
+  if (!(total > 0.0)) return fail(DLC_ERR_NO_QUORUM, "all learner weights are zero (no quorum)");
+  dlc::MergeArgs a;
+  std::memset(&a, 0, sizeof(a));
+  int32_t kp = 0;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (weights[i] > 0.0) {
+      a.learner[kp] = i;
+      a.w_hat[kp] = weights[i] / total;
+      ++kp;
+    }
+  }
+  a.theta_g = theta_global;
+  a.momentum = momentum;
+  a.codes = codes;
+  a.codebook = codebook;
+  a.stride = learner_stride;
+  a.n_present = kp;
+  a.lr = lr;
+  a.beta = beta;
+  const Partition p = make_partition(tensors, n_tensors);
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  for (const dlc::LaunchGeom& g : p.launches) {
+    hipError_t e = dlc::launch_merge(a, g, s);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  }
+  return ok();
+}
+
+const char* dlc_last_error(void) { return g_last_error.c_str(); }
+
+const char* dlc_version(void) { return "dlc 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Internal launch descriptors shared by the host orchestration and the gfx950 kernels.
+//
+// A call's tensors are processed in launches of at most kMaxTensorsPerLaunch
+// tensors.  Every launch carries its tensor descriptors in the kernel arguments
+// (no device-side tables, no host-to-device copies).  Within a launch each tensor
+// owns a contiguous run of blocks; block j of tensor t covers tiles
+// [j * tiles_per_block, (j + 1) * tiles_per_block) of that tensor only, so every
+// block's partial statistics / histogram belong to exactly one tensor and sit in
+// the workspace slot slot_base + blockIdx.x.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace dlc {
+
+constexpr int kBuckets = 256;
+constexpr int kMaxLearners = 64;
+constexpr int kMaxTensorsPerLaunch = 64;
+constexpr int kVec = 16;                  // elements per thread per tile (4 x float4)
+constexpr int kBlock = 256;               // threads per block
+constexpr int kTile = kBlock * kVec;      // elements per tile
+constexpr int kLearnerChunk = 16;         // learners per quantize launch
+
+struct TensorDesc {
+  int64_t offset;       // into theta_global / momentum
+  int64_t loffset;      // into each learner row
+  int64_t numel;
+  int32_t block_first;  // first block of this tensor within the launch
+  int32_t pad;
+};
+
+struct LaunchGeom {
+  int32_t n_tensors;        // tensors in this launch
+  int32_t t_base;           // call-level index of the launch's first tensor
+  int32_t n_tensors_call;   // tensors in the whole call (row length of range / codebook)
+  int32_t n_blocks;         // blocks in this launch
+  int32_t tiles_per_block;
+  int32_t slot_base;        // workspace slot of block 0
+  TensorDesc t[kMaxTensorsPerLaunch];
+};
+
+struct QuantArgs {
+  const float* theta_g;
+  const float* theta_L;
+  int64_t stride;           // learner row length (elements)
+  int32_t n_present;        // present learners in the call
+  int32_t k_base;           // first present-learner position handled by this launch
+  int32_t k_count;          // present learners handled by this launch (<= kLearnerChunk)
+  int32_t learner[kMaxLearners];  // present position -> learner index
+  float4* range;            // [n_learners][n_tensors_call] {lo, hi, wd, mean}
+  uint8_t* codes;           // [n_learners][stride]
+  float* codebook;          // [n_learners][n_tensors_call][256]
+  double2* part_stats;      // [slot][n_present] {sum(d), sum(d^2)}, d = Delta - shift
+  double* part_sum;         // [slot][n_present][256]
+  uint32_t* part_cnt;       // [slot][n_present][256]
+};
+
+struct MergeArgs {
+  float* theta_g;
+  float* momentum;
+  const uint8_t* codes;
+  const float* codebook;
+  int64_t stride;
+  int32_t n_present;
+  int32_t learner[kMaxLearners];
+  double w_hat[kMaxLearners];
+  double lr;
+  double beta;
+};
+
+// Kernel launchers (dlc_kernels.hip).  Each returns hipSuccess or the launch error.
+hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
+hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
+hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
+hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
+
+}  // namespace dlc

@@ -1,0 +1,180 @@
+/*
+ * dlc.h -- C ABI of the DiLoCo outer-step merge on one gfx950 GPU.
+ *
+ * One outer step over one fragment of a model is two calls:
+ *   dlc_quantize          learner side: pseudo-gradient, per-tensor statistics,
+ *                         6-sigma clip, 256-bucket uint8 codes and a codebook of
+ *                         per-bucket means, for every present learner;
+ *   dlc_merge_outer_step  syncer side: dequantize every learner, take the weighted
+ *                         mean in floating point, apply the Nesterov outer step.
+ * dlc_quantize is also available as its two stages (dlc_quantize_range, then
+ * dlc_quantize_encode) for callers that time or pin them separately, and
+ * dlc_fragment_plan splits a model into balanced fragments.
+ *
+ * Sources:
+ *   INTELLECT-1 reading notes ("Training a 10B Model Across 3 Continents"),
+ *     section 3.2 (worked example, steps 4-7), section 4.1 (uniform quantization
+ *     with clipping), section 4.2 (quantize for transport only; accumulate in
+ *     floating point, since Q(a) + Q(b) != Q(a + b));
+ *   Decoupled DiLoCo digest ("Resilient, Distributed AI Training at Scale"),
+ *     section "architecture" item 4 (P = 24 fragments from greedy bin-packing of
+ *     whole tensors) and "fault tolerance" items 1 and 3 (minimum quorum,
+ *     weighted merge).
+ *
+ * Conventions shared by every call
+ *   - Status: 0 = DLC_OK, negative = error.  The message of the last error on the
+ *     calling thread is returned by dlc_last_error().  No exception crosses the ABI.
+ *   - Ownership: every buffer is owned by the caller.  The library allocates and
+ *     frees no memory, keeps no state between calls and never synchronizes the
+ *     stream.  Device pointers must be on the current HIP device.
+ *   - Execution: work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream).  Argument errors are returned before anything is enqueued; a failed
+ *     launch returns DLC_ERR_HIP.  Two calls in flight at once must not share any
+ *     output buffer or workspace.
+ *   - Layout: a call covers n_tensors tensors (a fragment).  Tensor t occupies
+ *     elements [offset, offset + numel) of theta_global / momentum and elements
+ *     [loffset, loffset + numel) of every learner row of theta_learners and codes
+ *     (row i starts at i * learner_stride).  Per-(learner, tensor) outputs are
+ *     indexed [learner][t] with the call's tensor index t in 0..n_tensors-1 and the
+ *     learner's own index i in 0..n_learners-1.
+ *   - Alignment: device base pointers 256-byte aligned; offset, loffset and
+ *     learner_stride multiples of 64 elements; numel >= 1 (any value; tails are
+ *     handled on the device).  Tensor ranges must not overlap, in theta_global nor
+ *     within a learner row.
+ *   - Limits: 1 <= n_learners <= DLC_MAX_LEARNERS; n_tensors >= 1.
+ */
+#ifndef DLC_H
+#define DLC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLC_OK 0
+#define DLC_ERR_INVALID_ARGUMENT (-1)
+#define DLC_ERR_ALIGNMENT (-2)
+#define DLC_ERR_NO_QUORUM (-3)
+#define DLC_ERR_WORKSPACE (-4)
+#define DLC_ERR_HIP (-5)
+
+/* dlc_quantize flag: use the caller's `range` instead of computing it. */
+#define DLC_RANGE_GIVEN 1u
+
+#define DLC_MAX_LEARNERS 64
+#define DLC_N_BUCKETS 256
+#define DLC_ALIGN_ELEMS 64
+#define DLC_RANGE_FIELDS 4
+
+typedef struct dlc_tensor {
+    int64_t offset;   /* element offset into theta_global and momentum        */
+    int64_t loffset;  /* element offset into each learner row (theta, codes)  */
+    int64_t numel;    /* number of elements, >= 1                             */
+} dlc_tensor;
+
+/*
+ * dlc_fragment_plan -- greedy bin-packing of whole tensors into balanced
+ * fragments (Decoupled DiLoCo digest, "architecture" item 4, note 1; P = 24 there).
+ *
+ * Largest tensor first (ties: lower tensor index), each onto the fragment with the
+ * smallest load so far (ties: lower fragment id).  Pure host code.
+ *   numel          host [n_tensors], each >= 1
+ *   n_fragments    >= 1 (fragments may stay empty when n_tensors < n_fragments)
+ *   fragment_of    host out [n_tensors]: fragment id of each tensor
+ *   fragment_numel host out [n_fragments]: elements per fragment (may be NULL)
+ */
+int32_t dlc_fragment_plan(const int64_t* numel, int32_t n_tensors, int32_t n_fragments,
+                          int32_t* fragment_of, int64_t* fragment_numel);
+
+/*
+ * dlc_workspace_bytes -- device workspace that dlc_quantize / dlc_quantize_range /
+ * dlc_quantize_encode need for these tensors and up to n_learners present learners
+ * (per-block partial statistics and histograms).  Pure host code.
+ */
+int32_t dlc_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                            size_t* bytes);
+
+/*
+ * dlc_quantize_range -- stage A of quantization (INTELLECT-1 notes, section 3.2
+ * step 4 and section 4.1 steps 1-3).  For every present learner i and tensor t:
+ *   Delta = fl32(theta_global - theta_i)                       (never stored)
+ *   mu, sigma = mean and population std of Delta, accumulated in fp64
+ *   range[i][t] = { lo = fl32(mu - 6 sigma), hi = fl32(mu + 6 sigma),
+ *                   wd = fl32(12 sigma / 256), fl32(mu) }
+ *   theta_global    device fp32, read only
+ *   theta_learners  device fp32 [n_learners][learner_stride], read only
+ *   present         host uint8 [n_learners] (0 = absent: never read, outputs
+ *                   untouched) or NULL = all present; at least one present
+ *   range           device fp32 [n_learners][n_tensors][4], written
+ *   workspace       device, >= dlc_workspace_bytes(n_learners, ...) bytes
+ */
+int32_t dlc_quantize_range(const float* theta_global, const float* theta_learners,
+                           int64_t learner_stride, int32_t n_learners, const uint8_t* present,
+                           const dlc_tensor* tensors, int32_t n_tensors, float* range,
+                           void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * dlc_quantize_encode -- stage B of quantization (INTELLECT-1 notes, section 4.1
+ * steps 2-4).  Given range[i][t] = {lo, hi, wd, mean}:
+ *   code  = clip(floor(fl32(fl32(Delta - lo) / wd)), 0, 255)   (IEEE fp32, RNE)
+ *   x_c   = min(max(Delta, lo), hi)
+ *   codebook[i][t][c] = fl32(sum of x_c in bucket c / count)   (sums in fp64)
+ *                       or the midpoint fl32(lo + (c + 1/2) wd) for an empty bucket
+ *   If wd is not a normal fp32 (zero variance), every code is 0 and every
+ *   codebook entry is `mean`.
+ *   codes     device uint8 [n_learners][learner_stride], written at the tensors'
+ *             ranges of present learners
+ *   codebook  device fp32 [n_learners][n_tensors][256], written for present learners
+ */
+int32_t dlc_quantize_encode(const float* theta_global, const float* theta_learners,
+                            int64_t learner_stride, int32_t n_learners, const uint8_t* present,
+                            const dlc_tensor* tensors, int32_t n_tensors, const float* range,
+                            uint8_t* codes, float* codebook, void* workspace,
+                            size_t workspace_bytes, void* hip_stream);
+
+/*
+ * dlc_quantize -- dlc_quantize_range followed by dlc_quantize_encode.  With
+ * DLC_RANGE_GIVEN in `flags`, `range` is an input and only the encode stage runs.
+ */
+int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
+                     int64_t learner_stride, int32_t n_learners, const uint8_t* present,
+                     const dlc_tensor* tensors, int32_t n_tensors, uint8_t* codes,
+                     float* codebook, float* range, uint32_t flags, void* workspace,
+                     size_t workspace_bytes, void* hip_stream);
+
+/*
+ * dlc_merge_outer_step -- dequantize, weighted mean, Nesterov (INTELLECT-1 notes,
+ * section 3.2 steps 6-7 and section 4.2; Decoupled DiLoCo digest, "fault
+ * tolerance" items 1 and 3).  Per element of every tensor:
+ *   w_hat_i = w_i / sum_j w_j          (host, fp64, left-to-right sum)
+ *   g       = sum_i w_hat_i * codebook[i][t][code_i]   (learners in index order,
+ *             fp64 products and sums of the fp32 codebook values)
+ *   v      <- beta * v + g
+ *   theta  <- theta - lr * (g + beta * v)              (fp64, stored as fp32)
+ * Dequantized values are never added in code space.
+ *   theta_global, momentum  device fp32, updated in place at the tensors' ranges
+ *   codes, codebook         as written by dlc_quantize (read only)
+ *   weights                 host double [n_learners], finite and >= 0; 0 = absent
+ *                           (its codes and codebook are never read).  A zero total
+ *                           (no quorum) returns DLC_ERR_NO_QUORUM and changes nothing.
+ *   lr, beta                outer learning rate and momentum (0.7 and 0.9 on the pages)
+ *   flags                   reserved, must be 0
+ */
+int32_t dlc_merge_outer_step(float* theta_global, float* momentum, const uint8_t* codes,
+                             int64_t learner_stride, int32_t n_learners, const float* codebook,
+                             const double* weights, const dlc_tensor* tensors, int32_t n_tensors,
+                             double lr, double beta, uint32_t flags, void* hip_stream);
+
+/* Message of the last error on the calling thread ("" if none). */
+const char* dlc_last_error(void);
+
+/* Library version string. */
+const char* dlc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLC_H */

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+* libdlc.so loads and exports every function include/dlc.h declares;
+* dlc_fragment_plan (C++) equals the oracle's greedy bin-packing on every
+  parameter set, tensor for tensor;
+* every argument error is reported with its status code before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import diloco_outer_step_amd as dlc
+import oracle
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dlc.h")
+
+FAKE = 1 << 20  # a 256-byte aligned address that is never dereferenced (calls fail first)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dlc_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert len(names) >= 8
+    lib = ctypes.CDLL(dlc.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in dlc.h but not exported"
+    assert set(names) == set(dlc.EXPORTED)
+    assert "gfx950" in dlc.dlc_version()
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("DLC_OK", "DLC_ERR_INVALID_ARGUMENT", "DLC_ERR_ALIGNMENT", "DLC_ERR_NO_QUORUM",
+                 "DLC_ERR_WORKSPACE", "DLC_ERR_HIP", "DLC_MAX_LEARNERS", "DLC_N_BUCKETS",
+                 "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS"):
+        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
+        assert m and int(m.group(1)) == getattr(dlc, name), name
+
+
+@pytest.mark.parametrize("key", ["c2", "c3", "c4", "c5k1"])
+@pytest.mark.parametrize("p", [1, 7, 24])
+def test_fragment_plan_matches_oracle(key, p):
+    numel = [s.numel for s in workloads.config(key).tensors]
+    got = dlc.dlc_fragment_plan(numel, p)
+    want = oracle.fragment_plan(numel, p)
+    assert got[0] == list(want[0])
+    assert got[1] == list(want[1])
+
+
+def test_fragment_plan_small_cases():
+    assert dlc.dlc_fragment_plan([7, 5, 4, 3, 3, 2], 2) == ([0, 1, 1, 0, 1, 0], [12, 12])
+    assert dlc.dlc_fragment_plan([5, 1], 4) == ([0, 1], [5, 1, 0, 0])
+    with pytest.raises(dlc.DlcError):
+        dlc.dlc_fragment_plan([3, 0], 2)
+    with pytest.raises(dlc.DlcError):
+        dlc.dlc_fragment_plan([3], 0)
+
+
+def test_workspace_bytes_grows_with_learners():
+    t = [(0, 0, 1 << 22), (1 << 22, 1 << 22, 4096)]
+    a = dlc.dlc_workspace_bytes(1, t)
+    b = dlc.dlc_workspace_bytes(16, t)
+    assert 0 < a < b and a % 256 == 0 and b % 256 == 0
+    with pytest.raises(dlc.DlcError):
+        dlc.dlc_workspace_bytes(0, t)
+
+
+# --- argument errors: every call returns its status before touching the GPU ----------
+
+L = dlc._lib
+
+
+def tens(spec):
+    arr = (dlc._Tensor * len(spec))()
+    for i, (o, lo, n) in enumerate(spec):
+        arr[i].offset, arr[i].loffset, arr[i].numel = o, lo, n
+    return arr, len(spec)
+
+
+def quantize(k=2, spec=((0, 0, 4096),), stride=4096, theta=FAKE, present=None, ws_bytes=1 << 30,
+             ws=FAKE, codes=FAKE, flags=0):
+    arr, n = tens(spec)
+    pres = None
+    if present is not None:
+        buf = (ctypes.c_uint8 * k)(*present)
+        pres = ctypes.cast(buf, ctypes.c_void_p)
+    return L.dlc_quantize(theta, FAKE, stride, k, pres, arr, n, codes, FAKE, FAKE, flags, ws, ws_bytes, None)
+
+
+def merge(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), lr=0.7, beta=0.9, flags=0, theta=FAKE):
+    arr, n = tens(spec)
+    w = (ctypes.c_double * k)(*weights)
+    return L.dlc_merge_outer_step(theta, FAKE, FAKE, stride, k, FAKE, ctypes.cast(w, ctypes.c_void_p), arr, n,
+                                  lr, beta, flags, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: quantize(k=0), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(k=65), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(theta=None), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(theta=FAKE + 4), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: quantize(codes=FAKE + 16), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: quantize(spec=((32, 0, 4096),)), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: quantize(stride=4000), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: quantize(spec=((0, 0, 0),)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(spec=((0, 0, 4097),)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(spec=((0, 0, 128), (64, 128, 64)), stride=4096), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(spec=((0, 0, 128), (128, 64, 64)), stride=4096), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(present=[0, 0]), dlc.DLC_ERR_NO_QUORUM),
+    (lambda: quantize(ws_bytes=16), dlc.DLC_ERR_WORKSPACE),
+    (lambda: quantize(ws=None), dlc.DLC_ERR_WORKSPACE),
+    (lambda: quantize(flags=8), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: merge(weights=(0.0, 0.0)), dlc.DLC_ERR_NO_QUORUM),
+    (lambda: merge(weights=(1.0, -1.0)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: merge(weights=(1.0, float("nan"))), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: merge(weights=(1.0, float("inf"))), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: merge(lr=float("nan")), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: merge(flags=1), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: merge(theta=FAKE + 8), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: merge(k=0, weights=()), dlc.DLC_ERR_INVALID_ARGUMENT),
+])
+def test_argument_errors(call, code):
+    assert call() == code
+    assert dlc.dlc_last_error() != ""

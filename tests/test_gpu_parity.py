@@ -1,0 +1,137 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, element by
+element, on the same seeded inputs (tolerances in tests/parity.py)."""
+import numpy as np
+import pytest
+import torch
+
+import diloco_outer_step_amd as dlc
+import oracle
+import workloads
+from tests import parity
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+RAGGED = [1, 63, 64, 65, 577, 4095, 4096, 4097, 12289, 100003]
+
+
+def case_inputs(name):
+    if name == "c1":
+        cfg = workloads.config("c1")
+        return workloads.fragment_inputs(cfg, [0], DEV)
+    if name == "ragged_k3":
+        cfg = workloads.custom("ragged", RAGGED, 3)
+        return workloads.fragment_inputs(cfg, list(range(len(RAGGED))), DEV)
+    if name == "c2_median_fragment":
+        cfg = workloads.config("c2")
+        frag, loads = oracle.fragment_plan([s.numel for s in cfg.tensors], 24)
+        order = sorted(range(24), key=lambda p: (loads[p], p))
+        p = order[12]
+        ids = [t for t, f in enumerate(frag) if f == p]
+        return workloads.fragment_inputs(cfg, ids, DEV, fragment=p)
+    if name == "many_tensors_k20":
+        sizes = [4096] * 70 + [64 * 1000 + 64] * 10 + [5000]
+        cfg = workloads.custom("many", sizes, 20, delta="laplace", delta_scale=7e-4)
+        return workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV)
+    if name == "absent_k16_const":
+        sizes = [4096] * 6 + [1 << 16] * 3
+        kinds = ["vector", "const", "const", "vector", "const", "vector", "matrix", "matrix", "matrix"]
+        cfg = workloads.custom("absent", sizes, 16, delta="laplace", delta_scale=7e-4, absent_p=0.25, kinds=kinds)
+        return workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV, fragment=3)
+    raise KeyError(name)
+
+
+CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const"]
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_pinned_range_bit_exact(name):
+    """Given the oracle's (lo, hi, wd, mean), codes, codebooks, theta and momentum agree."""
+    inp = case_inputs(name)
+    orc = parity.oracle_step(inp)
+    r, given = parity.oracle_ranges_tensor(orc, inp)
+    gpu = parity.gpu_step(inp, given_range=r.to(DEV))
+    rep = parity.compare(gpu, orc, inp, pinned=True)
+    print(f"[{name} pinned] {rep}")
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_end_to_end(name):
+    inp = case_inputs(name)
+    orc = parity.oracle_step(inp)
+    gpu = parity.gpu_step(inp)
+    rep = parity.compare(gpu, orc, inp, pinned=False)
+    print(f"[{name} e2e] {rep}")
+
+
+def test_single_learner_weight_one():
+    cfg = workloads.custom("k1", [1 << 20, 333], 1)
+    inp = workloads.fragment_inputs(cfg, [0, 1], DEV)
+    gpu = parity.gpu_step(inp, lr=1.0, beta=0.0)
+    orc = parity.oracle_step(inp, lr=1.0, beta=0.0)
+    parity.compare(gpu, orc, inp, pinned=False)
+    # g = cb[code] exactly, so theta_new = fl32(theta_g - cb[code])
+    codes = parity.host(gpu["codes"])[0]
+    cb = parity.host(gpu["codebook"])[0]
+    tg = parity.host(inp.theta_g)
+    for t, (off, loff, n) in enumerate(inp.tensors):
+        want = (tg[off:off + n].astype(np.float64) - cb[t][codes[loff:loff + n]].astype(np.float64)).astype(np.float32)
+        assert np.array_equal(parity.host(gpu["theta"])[off:off + n], want)
+
+
+def test_stages_equal_fused_and_deterministic():
+    inp = case_inputs("ragged_k3")
+    k, stride = inp.theta_L.shape
+    t = len(inp.tensors)
+    a = parity.gpu_step(inp, merge=False)
+    b = parity.gpu_step(inp, merge=False)
+    codes, cb, rng = dlc.outputs_for(k, stride, t, DEV)
+    ws = dlc.alloc_workspace(k, inp.tensors, DEV)
+    dlc.dlc_quantize_range(inp.theta_g, inp.theta_L, inp.tensors, rng, ws)
+    dlc.dlc_quantize_encode(inp.theta_g, inp.theta_L, inp.tensors, rng, codes, cb, ws)
+    torch.cuda.synchronize()
+    for x in (b, dict(codes=codes, codebook=cb, range=rng)):
+        assert torch.equal(a["range"], x["range"])
+        for i in range(k):
+            for (o, lo, n) in inp.tensors:
+                assert torch.equal(a["codes"][i, lo:lo + n], x["codes"][i, lo:lo + n])
+        u = parity.ulp_distance(parity.host(a["codebook"]), parity.host(x["codebook"]))
+        assert u.max() <= 1
+
+
+def test_no_quorum_changes_nothing():
+    inp = case_inputs("ragged_k3")
+    k, stride = inp.theta_L.shape
+    codes, cb, rng = dlc.outputs_for(k, stride, len(inp.tensors), DEV)
+    theta = inp.theta_g.clone()
+    mom = inp.momentum.clone()
+    with pytest.raises(dlc.NoQuorumError):
+        dlc.dlc_merge_outer_step(theta, mom, codes, cb, [0.0] * k, inp.tensors)
+    torch.cuda.synchronize()
+    assert torch.equal(theta, inp.theta_g) and torch.equal(mom, inp.momentum)
+
+
+def test_fragments_equal_whole_set():
+    """Merging per fragment (any order) equals one call over every tensor, bit for bit;
+    tensors outside a fragment are untouched."""
+    cfg = workloads.config("c2")
+    ids = list(range(1, 19))  # two layers
+    inp = workloads.fragment_inputs(cfg, ids, DEV)
+    whole = parity.gpu_step(inp)
+    frag, _ = oracle.fragment_plan([n for _, _, n in inp.tensors], 3)
+    theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+    k, stride = inp.theta_L.shape
+    for p in (1, 2, 0):
+        sel = [d for d, f in zip(inp.tensors, frag) if f == p]
+        codes, cb, rng = dlc.outputs_for(k, stride, len(sel), DEV)
+        ws = dlc.alloc_workspace(k, sel, DEV)
+        before = theta.clone()
+        dlc.dlc_quantize(theta, inp.theta_L, sel, codes, cb, rng, ws)
+        dlc.dlc_merge_outer_step(theta, mom, codes, cb, inp.weights, sel)
+        torch.cuda.synchronize()
+        mask = torch.ones_like(theta, dtype=torch.bool)
+        for (o, lo, n) in sel:
+            mask[o:o + n] = False
+        assert torch.equal(theta[mask], before[mask])
+    assert torch.equal(theta, whole["theta"]) and torch.equal(mom, whole["momentum"])

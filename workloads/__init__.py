@@ -328,3 +328,13 @@ def fragment_inputs(cfg: Config, tensor_ids: Sequence[int], device, step: int = 
     w = [wi if p else 0.0 for wi, p in zip(w, pres)]
     tens = [(o, lo, cfg.tensors[t].numel) for o, lo, t in zip(offs, loffs, tensor_ids)]
     return StepInputs(theta_g, mom, theta_L, tens, w, pres, list(tensor_ids), stride)
+
+
+def custom(key: str, sizes: Sequence[int], n_learners: int, delta: str = "normal",
+           delta_scale: float = 1e-3, weights: str = "equal", absent_p: float = 0.0,
+           kinds: Optional[Sequence[str]] = None) -> Config:
+    """A parameter set of flat tensors of the given sizes (ragged sizes allowed)."""
+    kinds = kinds or ["matrix"] * len(sizes)
+    specs = tuple(TensorSpec(f"t{i}", (int(n),), k) for i, (n, k) in enumerate(zip(sizes, kinds)))
+    return Config(key, f"custom {len(sizes)} tensors, K={n_learners}", specs, n_learners, 1,
+                  delta, delta_scale, weights, absent_p=absent_p)
