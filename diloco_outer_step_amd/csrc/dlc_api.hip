@@ -41,12 +41,14 @@ struct Partition {
 
 // Split the call's tensors into launches of at most kMaxTensorsPerLaunch tensors;
 // each tensor gets ceil(tiles / tiles_per_block) blocks, tiles_per_block chosen
-// from the whole call so that the call has about kTargetBlocks blocks.
-Partition make_partition(const dlc_tensor* t, int32_t n) {
+// from the whole call so that the call has about kTargetBlocks blocks, and at
+// most max_tiles.
+Partition make_partition(const dlc_tensor* t, int32_t n, int64_t max_tiles) {
   Partition p;
   int64_t total_tiles = 0;
   for (int32_t i = 0; i < n; ++i) total_tiles += (t[i].numel + dlc::kTile - 1) / dlc::kTile;
-  const int64_t tpb = std::max<int64_t>(1, (total_tiles + kTargetBlocks - 1) / kTargetBlocks);
+  int64_t tpb = std::max<int64_t>(1, (total_tiles + kTargetBlocks - 1) / kTargetBlocks);
+  tpb = std::min(tpb, max_tiles);
   for (int32_t s = 0; s < n; s += dlc::kMaxTensorsPerLaunch) {
     dlc::LaunchGeom g;
     std::memset(&g, 0, sizeof(g));
@@ -72,19 +74,20 @@ Partition make_partition(const dlc_tensor* t, int32_t n) {
   return p;
 }
 
+constexpr int64_t kUnlimitedTiles = int64_t(1) << 40;
+
 struct WorkspaceLayout {
-  size_t stats = 0, sum = 0, cnt = 0, total = 0;
+  size_t stats = 0, hist = 0, total = 0;
 };
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
-WorkspaceLayout workspace_layout(int64_t n_slots, int32_t n_learners) {
+// Workspace: per-block statistics partials, then per-block packed histograms.
+WorkspaceLayout workspace_layout(int64_t stats_slots, int64_t hist_slots, int32_t n_learners) {
   WorkspaceLayout w;
-  const size_t per = (size_t)n_slots * (size_t)n_learners;
   w.stats = 0;
-  w.sum = round256(per * sizeof(double) * 2);
-  w.cnt = w.sum + round256(per * dlc::kBuckets * sizeof(double));
-  w.total = w.cnt + round256(per * dlc::kBuckets * sizeof(uint32_t));
+  w.hist = round256((size_t)stats_slots * (size_t)n_learners * sizeof(double) * 2);
+  w.total = w.hist + round256((size_t)hist_slots * (size_t)n_learners * dlc::kBuckets * sizeof(uint64_t));
   return w;
 }
 
@@ -121,7 +124,8 @@ int32_t check_tensors(const dlc_tensor* t, int32_t n, int64_t learner_stride, bo
 
 struct Common {
   dlc::QuantArgs args;
-  Partition part;
+  Partition part_stats;   // statistics pass (range stage)
+  Partition part_enc;     // encode pass: blocks capped at kMaxEncodeTiles tiles
   hipStream_t stream;
 };
 
@@ -143,8 +147,9 @@ int32_t setup_quant(Common& c, const float* theta_global, const float* theta_lea
     if (present == nullptr || present[i] != 0) c.args.learner[kp++] = i;
   }
   if (kp == 0) return fail(DLC_ERR_NO_QUORUM, "no learner is present");
-  c.part = make_partition(tensors, n_tensors);
-  const WorkspaceLayout wl = workspace_layout(c.part.n_slots, kp);
+  c.part_stats = make_partition(tensors, n_tensors, kUnlimitedTiles);
+  c.part_enc = make_partition(tensors, n_tensors, dlc::kMaxEncodeTiles);
+  const WorkspaceLayout wl = workspace_layout(c.part_stats.n_slots, c.part_enc.n_slots, kp);
   if (workspace == nullptr || workspace_bytes < wl.total)
     return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(wl.total) + " bytes");
   if (!aligned256(workspace)) return fail(DLC_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
@@ -154,8 +159,7 @@ int32_t setup_quant(Common& c, const float* theta_global, const float* theta_lea
   c.args.stride = learner_stride;
   c.args.n_present = kp;
   c.args.part_stats = reinterpret_cast<double2*>(ws + wl.stats);
-  c.args.part_sum = reinterpret_cast<double*>(ws + wl.sum);
-  c.args.part_cnt = reinterpret_cast<uint32_t*>(ws + wl.cnt);
+  c.args.part_hist = reinterpret_cast<uint64_t*>(ws + wl.hist);
   c.stream = static_cast<hipStream_t>(hip_stream);
   return DLC_OK;
 }
@@ -165,10 +169,14 @@ int32_t hip_fail(hipError_t e, const char* what) {
 }
 
 int32_t run_range(Common& c) {
-  for (const dlc::LaunchGeom& g : c.part.launches) {
-    for (int32_t k0 = 0; k0 < c.args.n_present; k0 += dlc::kLearnerChunk) {
+  for (const dlc::LaunchGeom& g : c.part_stats.launches) {
+    // Learners in balanced chunks of at most kStatsChunk (e.g. 14 -> 7 + 7).
+    const int32_t n_chunks = (c.args.n_present + dlc::kStatsChunk - 1) / dlc::kStatsChunk;
+    for (int32_t ci = 0, k0 = 0; ci < n_chunks; ++ci) {
+      const int32_t kc = (c.args.n_present - k0) / (n_chunks - ci);
       c.args.k_base = k0;
-      c.args.k_count = std::min(dlc::kLearnerChunk, c.args.n_present - k0);
+      c.args.k_count = kc;
+      k0 += kc;
       hipError_t e = dlc::launch_stats(c.args, g, c.stream);
       if (e != hipSuccess) return hip_fail(e, "stats kernel launch");
     }
@@ -179,7 +187,7 @@ int32_t run_range(Common& c) {
 }
 
 int32_t run_encode(Common& c) {
-  for (const dlc::LaunchGeom& g : c.part.launches) {
+  for (const dlc::LaunchGeom& g : c.part_enc.launches) {
     for (int32_t k0 = 0; k0 < c.args.n_present; k0 += dlc::kLearnerChunk) {
       c.args.k_base = k0;
       c.args.k_count = std::min(dlc::kLearnerChunk, c.args.n_present - k0);
@@ -225,8 +233,9 @@ int32_t dlc_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32
     return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
   int32_t rc = check_tensors(tensors, n_tensors, 0, false);
   if (rc != DLC_OK) return rc;
-  const Partition p = make_partition(tensors, n_tensors);
-  *bytes = workspace_layout(p.n_slots, n_learners).total;
+  const Partition ps = make_partition(tensors, n_tensors, kUnlimitedTiles);
+  const Partition pe = make_partition(tensors, n_tensors, dlc::kMaxEncodeTiles);
+  *bytes = workspace_layout(ps.n_slots, pe.n_slots, n_learners).total;
   return ok();
 }
 
@@ -328,7 +337,7 @@ int32_t dlc_merge_outer_step(float* theta_global, float* momentum, const uint8_t
   a.n_present = kp;
   a.lr = lr;
   a.beta = beta;
-  const Partition p = make_partition(tensors, n_tensors);
+  const Partition p = make_partition(tensors, n_tensors, kUnlimitedTiles);
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   for (const dlc::LaunchGeom& g : p.launches) {
     hipError_t e = dlc::launch_merge(a, g, s);

@@ -22,7 +22,17 @@ constexpr int kMaxTensorsPerLaunch = 64;
 constexpr int kVec = 16;                  // elements per thread per tile (4 x float4)
 constexpr int kBlock = 256;               // threads per block
 constexpr int kTile = kBlock * kVec;      // elements per tile
-constexpr int kLearnerChunk = 16;         // learners per quantize launch
+constexpr int kLearnerChunk = 16;         // learners per encode launch
+// Bucket histograms are packed 64-bit integers: bits 44..63 count elements, bits
+// 0..43 sum each element's position inside its bucket in units of wd * 2^-s
+// (s <= kHistFracBits), offset by kHistBias.  An encode block covers at most
+// kMaxEncodeTiles tiles of a tensor (2^17 elements per learner), so neither field
+// can overflow: 2^17 * 2^27 <= 2^44 and 2^17 < 2^20.
+constexpr int kMaxEncodeTiles = 32;
+constexpr int kHistFracBits = 26;
+constexpr int kHistBias = 1 << 13;
+constexpr int kHistCountShift = 44;
+constexpr int kStatsChunk = 8;            // learners per statistics launch (register accumulators)
 
 struct TensorDesc {
   int64_t offset;       // into theta_global / momentum
@@ -54,8 +64,7 @@ struct QuantArgs {
   uint8_t* codes;           // [n_learners][stride]
   float* codebook;          // [n_learners][n_tensors_call][256]
   double2* part_stats;      // [slot][n_present] {sum(d), sum(d^2)}, d = Delta - shift
-  double* part_sum;         // [slot][n_present][256]
-  uint32_t* part_cnt;       // [slot][n_present][256]
+  uint64_t* part_hist;      // [slot][n_present][256] packed (count, position sum)
 };
 
 struct MergeArgs {

@@ -1,10 +1,10 @@
 // gfx950 kernels of the DiLoCo outer-step merge.
 //
-// Three streaming passes over HBM per outer step, plus two tiny finalizers:
+// Three streaming passes over HBM per outer step, plus two small finalizers:
 //   k_stats     per-(learner, tensor) partial sum(d), sum(d^2) of d = Delta - shift, fp64
 //   k_range     per-(learner, tensor) mu, sigma -> {lo, hi, wd, mean} (fp64 -> fp32)
 //   k_encode    Delta -> clip -> bucket -> uint8 code (16-byte stores) + LDS histogram
-//               of (sum of clipped values in fp64, count) per learner
+//               of (count, fixed-point position sum) per bucket and learner
 //   k_codebook  per-(learner, tensor, bucket) mean of the clipped values -> fp32
 //   k_merge     dequantize K learners through fp64 LDS tables w_hat_i * codebook_i,
 //               sum, Nesterov update of theta and momentum, every byte read once
@@ -14,12 +14,16 @@
 // merge follows section 3.2 steps 6-7 and section 4.2 (dequantize, accumulate in
 // floating point, Nesterov with lr 0.7 / momentum 0.9).
 //
-// Every tile is kTile = 4096 elements of one tensor; thread tid owns the float4s
-// q = j * kBlock + tid (j = 0..3), so each load instruction of a wave reads 1 KB
-// of consecutive bytes.  Floating point contraction is off for this file: every
-// operation that has to match the fp32/fp64 definition bit for bit is written as
-// separate IEEE operations; the only fused multiply-add is the explicit one that
-// accumulates sum(d^2).
+// Memory layout of a tile: kTile = 4096 elements of one tensor; wave w of the block
+// owns elements [1024 w, 1024 w + 1024) and each load instruction of a wave reads
+// 1 KB of consecutive bytes.  Streaming reads and writes are non-temporal (each
+// byte is touched once per pass and the working set is far larger than the caches).
+// The next learner's tile is loaded while the current one is processed.
+//
+// Floating point contraction is off for this file: every operation that has to
+// match the fp32/fp64 definition bit for bit is written as separate IEEE
+// operations; the only fused multiply-add is the explicit one that accumulates
+// sum(d^2).
 #include "dlc_internal.h"
 
 #include <cfloat>
@@ -27,7 +31,11 @@
 namespace dlc {
 namespace {
 
+typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = kBlock / 64;
+constexpr int kHistBytes = kBuckets * 8;  // per learner: 256 packed 64-bit bucket accumulators
 
 struct Span {
   int t;          // tensor index within the launch
@@ -57,11 +65,19 @@ __device__ __forceinline__ int tensor_block_end(const LaunchGeom& g, int t) {
   return t + 1 < g.n_tensors ? g.t[t + 1].block_first : g.n_blocks;
 }
 
-// 16 floats of a full tile (4 coalesced float4 loads).
+// Thread -> element mapping inside a tile: wave w owns the contiguous elements
+// [1024 w, 1024 w + 1024); lane L of that wave holds float4 number 64 j + L of
+// the chunk for j = 0..3.  Every load instruction of a wave reads 1 KB of
+// consecutive bytes, and the wave's 1024 one-byte codes form one contiguous 1 KB
+// block.
+__device__ __forceinline__ int f4_index(int tid, int j) { return (tid & ~63) * 4 + j * 64 + (tid & 63); }
+
+// 16 floats of a full tile, 4 coalesced non-temporal float4 loads.
 __device__ __forceinline__ void load_full(const float* __restrict__ p, int tid, float (&v)[kVec]) {
+  const vf4* q = reinterpret_cast<const vf4*>(p);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float4 x = *reinterpret_cast<const float4*>(p + 4 * (j * kBlock + tid));
+    const vf4 x = __builtin_nontemporal_load(q + f4_index(tid, j));
     v[4 * j + 0] = x.x;
     v[4 * j + 1] = x.y;
     v[4 * j + 2] = x.z;
@@ -69,21 +85,33 @@ __device__ __forceinline__ void load_full(const float* __restrict__ p, int tid, 
   }
 }
 
-// 16 floats of a tail tile: element e valid iff base_rel + e < n (n elements left).
+__device__ __forceinline__ int64_t elem_index(int tid, int j, int c) { return 4 * (int64_t)f4_index(tid, j) + c; }
+
+__device__ __forceinline__ bool tail_valid(int tid, int j, int c, int64_t n) { return elem_index(tid, j, c) < n; }
+
+// 16 floats of a tail tile: element e valid iff its index is below n.
 __device__ __forceinline__ void load_tail(const float* __restrict__ p, int tid, int64_t n,
                                           float (&v)[kVec]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int64_t e = 4 * (j * kBlock + tid) + c;
-      v[4 * j + c] = e < n ? p[e] : 0.0f;
+      v[4 * j + c] = tail_valid(tid, j, c, n) ? p[elem_index(tid, j, c)] : 0.0f;
     }
   }
 }
 
-__device__ __forceinline__ bool tail_valid(int tid, int j, int c, int64_t n) {
-  return (int64_t)(4 * (j * kBlock + tid) + c) < n;
+__device__ __forceinline__ void store_full(float* __restrict__ p, int tid, const float (&v)[kVec]) {
+  vf4* q = reinterpret_cast<vf4*>(p);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vf4 x;
+    x.x = v[4 * j + 0];
+    x.y = v[4 * j + 1];
+    x.z = v[4 * j + 2];
+    x.w = v[4 * j + 3];
+    __builtin_nontemporal_store(x, q + f4_index(tid, j));
+  }
 }
 
 template <typename T>
@@ -93,68 +121,97 @@ __device__ __forceinline__ T wave_sum(T v) {
   return v;
 }
 
+__device__ __forceinline__ const float* learner_row(const QuantArgs& a, int k, const TensorDesc& td) {
+  return a.theta_L + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset;
+}
+
 // ---------------------------------------------------------------------------
 // k_stats: partial moments about a per-(learner, tensor) shift.
 //
 // shift = Delta at the tensor's first element, so sum(d) and sum(d^2) stay small
 // and var = sum(d^2)/n - (sum(d)/n)^2 loses nothing in fp64.  Each block covers
 // one tensor; its per-learner partial sums go to workspace slot slot_base + block.
+// Accumulators live in registers (KC learners, unrolled).
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void stats_accumulate(const float (&gv)[kVec], const float (&lv)[kVec],
+                                                 double shift, double& s1, double& s2) {
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    const double d = (double)(gv[e] - lv[e]) - shift;
+    s1 += d;
+    s2 = __fma_rn(d, d, s2);
+  }
+}
+
+// Learner tiles stream through a ring of kStatsRing register buffers: the tile of
+// learner item i + kStatsRing - 1 is requested while item i is accumulated.  KC is
+// a multiple of the ring size so ring slots are compile-time constants across
+// tiles; items beyond k_count re-request a valid tile and are not accumulated.
+// Every request is unconditional (clamped addresses), so the wait counts the
+// compiler derives stay exact and never drain the ring.
+constexpr int kStatsRing = 4;
+
 template <int KC>
 __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const LaunchGeom g) {
+  static_assert(KC % kStatsRing == 0, "KC must be a multiple of the ring size");
   const int tid = threadIdx.x;
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
   const float* __restrict__ tg = a.theta_g + td.offset;
   const int kc = a.k_count;
 
-  const float* tl[KC];
-  double shift[KC], s1[KC], s2[KC];
+  float shift[KC];  // Delta at element 0: an fp32 value, widened where used
+  double s1[KC], s2[KC];
   const float g0 = tg[0];
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
-    const int li = a.learner[a.k_base + (k < kc ? k : 0)];
-    tl[k] = a.theta_L + (int64_t)li * a.stride + td.loffset;
-    shift[k] = (double)(g0 - tl[k][0]);
+    const float* row = learner_row(a, k < kc ? k : kc - 1, td);
+    shift[k] = g0 - row[0];
     s1[k] = 0.0;
     s2[k] = 0.0;
   }
 
-  for (int64_t base = sp.begin; base < sp.end; base += kTile) {
-    const int64_t n = sp.end - base;
-    float gv[kVec];
-    if (n >= kTile) {
-      load_full(tg + base, tid, gv);
+  const int64_t n_full = (sp.end - sp.begin) / kTile;
+  if (n_full > 0) {
+    const int64_t last = sp.begin + (n_full - 1) * kTile;
+    float gv[kVec], gn[kVec], ring[kStatsRing][kVec];
+    load_full(tg + sp.begin, tid, gv);
+#pragma unroll
+    for (int i = 0; i < kStatsRing - 1; ++i) load_full(learner_row(a, i < kc ? i : kc - 1, td) + sp.begin, tid, ring[i]);
+    for (int64_t base = sp.begin; base <= last; base += kTile) {
+      const int64_t nbase = base < last ? base + kTile : last;
+      load_full(tg + nbase, tid, gn);
 #pragma unroll
       for (int k = 0; k < KC; ++k) {
-        if (k < kc) {
-          float lv[kVec];
-          load_full(tl[k] + base, tid, lv);
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) {
-            const double d = (double)(gv[e] - lv[e]) - shift[k];
-            s1[k] += d;
-            s2[k] = __fma_rn(d, d, s2[k]);
-          }
-        }
+        const int ip = k + kStatsRing - 1;
+        const int kl = ip < KC ? ip : ip - KC;
+        const int64_t pb = ip < KC ? base : nbase;
+        load_full(learner_row(a, kl < kc ? kl : kc - 1, td) + pb, tid, ring[ip % kStatsRing]);
+        if (k < kc) stats_accumulate(gv, ring[k % kStatsRing], (double)shift[k], s1[k], s2[k]);
       }
-    } else {
-      load_tail(tg + base, tid, n, gv);
 #pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        if (k < kc) {
-          float lv[kVec];
-          load_tail(tl[k] + base, tid, n, lv);
+      for (int e = 0; e < kVec; ++e) gv[e] = gn[e];
+    }
+  }
+  const int64_t full_end = sp.begin + n_full * kTile;
+  if (full_end < sp.end) {
+    const int64_t n = sp.end - full_end;
+    float gv[kVec];
+    load_tail(tg + full_end, tid, n, gv);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+    for (int k = 0; k < KC; ++k) {
+      if (k < kc) {
+        float lv[kVec];
+        load_tail(learner_row(a, k, td) + full_end, tid, n, lv);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              if (tail_valid(tid, j, c, n)) {
-                const int e = 4 * j + c;
-                const double d = (double)(gv[e] - lv[e]) - shift[k];
-                s1[k] += d;
-                s2[k] = __fma_rn(d, d, s2[k]);
-              }
+        for (int j = 0; j < 4; ++j) {
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            if (tail_valid(tid, j, c, n)) {
+              const int e = 4 * j + c;
+              const double d = (double)(gv[e] - lv[e]) - (double)shift[k];
+              s1[k] += d;
+              s2[k] = __fma_rn(d, d, s2[k]);
             }
           }
         }
@@ -187,8 +244,9 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
 }
 
 // ---------------------------------------------------------------------------
-// k_range: one thread per (present learner, tensor of the launch).
-// Blocks of a tensor are summed in block order (deterministic).
+// k_range: one thread per (present learner, tensor of the launch).  The tensor's
+// block partials are summed in block order (deterministic); loads are issued
+// eight at a time ahead of the dependent adds.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void k_range(const QuantArgs a, const LaunchGeom g) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
@@ -197,11 +255,24 @@ __global__ __launch_bounds__(64) void k_range(const QuantArgs a, const LaunchGeo
   const int t = idx - k * g.n_tensors;
   const TensorDesc td = g.t[t];
   const int b0 = td.block_first, b1 = tensor_block_end(g, t);
+  const double2* p = a.part_stats + (size_t)(g.slot_base + b0) * a.n_present + k;
+  const int nb = b1 - b0;
   double S1 = 0.0, S2 = 0.0;
-  for (int b = b0; b < b1; ++b) {
-    const double2 p = a.part_stats[(size_t)(g.slot_base + b) * a.n_present + k];
-    S1 += p.x;
-    S2 += p.y;
+  int b = 0;
+  for (; b + 8 <= nb; b += 8) {
+    double2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(b + u) * a.n_present];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      S1 += v[u].x;
+      S2 += v[u].y;
+    }
+  }
+  for (; b < nb; ++b) {
+    const double2 v = p[(size_t)b * a.n_present];
+    S1 += v.x;
+    S2 += v.y;
   }
   const int li = a.learner[k];
   const float g0 = a.theta_g[td.offset];
@@ -224,140 +295,289 @@ __global__ __launch_bounds__(64) void k_range(const QuantArgs a, const LaunchGeo
 // ---------------------------------------------------------------------------
 // k_encode: codes + per-block LDS histogram for up to kLearnerChunk learners.
 //
-// Dynamic LDS: hsum[kc][256] (fp64), hcnt[kc][256] (u32), stage[kWaves][256] (u32).
-// Codes of a full tile are packed 4 per dword in the load layout, transposed
-// through a per-wave LDS stage, and written with 16-byte stores (16 lanes write
-// 256 consecutive bytes).
+// Bucket index.  The definition is c = clip(floor(fl32(fl32(x - lo) / wd)), 0, 255).
+// With r = fl32(1 / wd) and q' = fl32(t * r), t = fl32(x - lo), both q' and the
+// correctly rounded quotient q = fl32(t / wd) lie within 1.5 * 2^-24 relative of
+// the exact t / wd, so |q' - q| <= 3 * 2^-24 * |t / wd|.  Wherever the result is not
+// clamped (|t / wd| < 257) that is below 2^-14, so floor(q') = floor(q) whenever the
+// fractional part of q' is at least 2^-14 away from 0 and from 1.  Only those rare
+// elements (about 1 in 8000) take the exact IEEE division.
+//
+// Histogram: one 64-bit LDS atomic per element adds 2^44 (the count) plus the
+// element's position inside its bucket as a fixed-point integer (low 44 bits),
+// see hist_frac_bits.  Integer sums make the histogram exact and independent of
+// the order of the atomics.  Codes of a full tile are packed 4
+// per dword in the load layout, transposed through a per-wave LDS stage, and
+// written with 16-byte stores: one store instruction writes the wave's 1 KB of
+// codes contiguously.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t bucket_of(float x, float lo, float wd) {
-  const float t = x - lo;
-  const float q = t / wd;  // IEEE fp32 division (correctly rounded)
-  const float c = fminf(fmaxf(floorf(q), 0.0f), 255.0f);
-  return (uint32_t)c;
+__device__ __forceinline__ float uniform_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
+
+__device__ __forceinline__ double uniform_f64(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Fraction bits s of the packed bucket-position sums for one (learner, tensor).
+// An element of bucket c contributes q = round((x_c - lo) * 2^s / wd - c * 2^s).
+// For buckets 0..254, q lies within [-2^12, 2^s + 2^12] (the fp32 bucket index
+// can misplace x by at most 3 * 2^-24 * 257 bucket widths); bucket 255 also holds
+// the values up to hi, i.e. q <= ((hi - lo) / wd - 255) * 2^s.  s is the largest
+// value <= kHistFracBits that keeps q + kHistBias below 2^27 (normally 26).
+__device__ __forceinline__ int hist_frac_bits(float lo, float hi, float wd) {
+  const double ext = ((double)hi - (double)lo) / (double)wd - 255.0;
+  const double top = ext > 1.0 ? ext : 1.0;
+  int s = kHistFracBits;
+  while (s > 0 && top * (double)(1ll << s) + 2.0 * kHistBias >= (double)(1ll << 27)) --s;
+  return s;
+}
+
+// Per-learner encode parameters, staged in LDS once per block.
+struct EncodePar {
+  float lo, hi, wd, rcp;  // clip range, bucket width, fl32(1 / wd)
+  double scale;           // 2^s / wd
+  double neg_lo_scale;    // -lo * 2^s / wd
+  double two_s;           // 2^s
+  double pad;
+};
+
+__device__ __forceinline__ EncodePar make_encode_par(float4 r) {
+  EncodePar p;
+  p.lo = r.x;
+  p.hi = r.y;
+  p.wd = r.z;
+  p.rcp = 0.0f;
+  p.scale = p.neg_lo_scale = p.two_s = p.pad = 0.0;
+  if (r.z >= FLT_MIN) {
+    p.rcp = 1.0f / r.z;
+    const int s = hist_frac_bits(r.x, r.y, r.z);
+    p.two_s = (double)(1ll << s);
+    p.scale = p.two_s / (double)r.z;
+    p.neg_lo_scale = -(double)r.x * p.scale;
+  }
+  return p;
+}
+
+template <bool FULL>
+__device__ __forceinline__ void encode_tile(uint64_t* __restrict__ hist, uint32_t* __restrict__ st,
+                                            uint8_t* __restrict__ cp, const float (&gv)[kVec],
+                                            const float (&lv)[kVec], const EncodePar& par_lds, int tid,
+                                            int64_t n) {
+  // The parameters are the same for every lane: keep them in scalar registers.
+  const float lo = uniform_f32(par_lds.lo), hi = uniform_f32(par_lds.hi), wd = uniform_f32(par_lds.wd);
+  const float rcp = uniform_f32(par_lds.rcp);
+  const double scale = uniform_f64(par_lds.scale), neg_lo_scale = uniform_f64(par_lds.neg_lo_scale);
+  const double neg_two_s = -uniform_f64(par_lds.two_s);
+  uint32_t packed[4] = {0u, 0u, 0u, 0u};
+  if (wd >= FLT_MIN) {  // otherwise (zero variance) every code is 0 and no histogram is needed
+    constexpr float kNear = 0.5f - 0x1p-14f;
+    float x[kVec], fq[kVec];
+    bool near_any = false;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      x[e] = gv[e] - lv[e];
+      const float q = (x[e] - lo) * rcp;
+      fq[e] = floorf(q);
+      near_any |= fabsf((q - fq[e]) - 0.5f) > kNear;
+    }
+    // Rare: some element of the wave lies within 2^-14 of a bucket edge; redo those
+    // with the correctly rounded division (one wave-uniform branch per tile).
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near_any) != 0, 0)) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const float t = x[e] - lo;
+        const float q = t * rcp;
+        const bool near = fabsf((q - fq[e]) - 0.5f) > kNear;
+        const float exact = floorf(t / wd);
+        fq[e] = near ? exact : fq[e];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t w = 0;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * j + c;
+        const float cf = __builtin_amdgcn_fmed3f(fq[e], 0.0f, 255.0f);
+        const uint32_t code = (uint32_t)cf;
+        if (FULL || tail_valid(tid, j, c, n)) {
+          // position of the clipped value inside its bucket, fixed point
+          const double xc = (double)__builtin_amdgcn_fmed3f(x[e], lo, hi);
+          const double off = __fma_rn((double)cf, neg_two_s, neg_lo_scale);
+          const int32_t q = (int32_t)__builtin_rint(__fma_rn(xc, scale, off));
+          const uint64_t add = ((uint64_t)1 << kHistCountShift) + (uint32_t)(q + kHistBias);
+          atomicAdd(reinterpret_cast<unsigned long long*>(hist + code), (unsigned long long)add);
+        }
+        w |= code << (8 * c);
+      }
+      packed[j] = w;
+    }
+  }
+  if (FULL) {
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) st[j * 64 + lane] = packed[j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const vu4 v = *reinterpret_cast<const vu4*>(st + 4 * lane);
+    *reinterpret_cast<vu4*>(cp + 1024 * wave + 16 * lane) = v;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (tail_valid(tid, j, c, n)) cp[elem_index(tid, j, c)] = (uint8_t)(packed[j] >> (8 * c));
+      }
+    }
+  }
+}
+
+// Learner tiles stream through a ring of kEncRing register buffers (request
+// item i + kEncRing - 1 while encoding item i).  Items per tile are padded to a
+// multiple of the ring so slots are compile-time constants; padded items request
+// a valid tile again and encode nothing.  Requests are unconditional so that the
+// compiler's wait counts stay exact.  Per-learner {lo, hi, wd, 1/wd} are staged
+// in LDS once per block.
+constexpr int kEncRing = 3;
 
 __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const LaunchGeom g) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int kc = a.k_count;
-  double* hsum = reinterpret_cast<double*>(smem);
-  uint32_t* hcnt = reinterpret_cast<uint32_t*>(hsum + kc * kBuckets);
-  uint32_t* stage = hcnt + kc * kBuckets;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  for (int i = tid; i < kc * kBuckets; i += kBlock) {
-    hsum[i] = 0.0;
-    hcnt[i] = 0u;
-  }
-  __syncthreads();
+  uint64_t* hist = reinterpret_cast<uint64_t*>(smem);
+  uint32_t* stage = reinterpret_cast<uint32_t*>(smem + kc * kHistBytes);
+  EncodePar* par = reinterpret_cast<EncodePar*>(stage + kWaves * 256);
+  const int tid = threadIdx.x, wave = tid >> 6;
 
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
-  const float* __restrict__ tg = a.theta_g + td.offset;
   const size_t rrow = (size_t)g.t_base + sp.t;
+  for (int i = tid; i < kc * (kHistBytes / 8); i += kBlock) reinterpret_cast<uint64_t*>(smem)[i] = 0;
+  if (tid < kc) par[tid] = make_encode_par(a.range[(size_t)a.learner[a.k_base + tid] * g.n_tensors_call + rrow]);
+  __syncthreads();
+
+  const float* __restrict__ tg = a.theta_g + td.offset;
   uint32_t* st = stage + wave * 256;
+  auto codes_of = [&](int k) {
+    return a.codes + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset;
+  };
 
-  for (int64_t base = sp.begin; base < sp.end; base += kTile) {
-    const int64_t n = sp.end - base;
-    const bool full = n >= kTile;
+  const int64_t n_full = (sp.end - sp.begin) / kTile;
+  if (n_full > 0) {
+    const int items = (kc + kEncRing - 1) / kEncRing * kEncRing;
+    const int64_t last = sp.begin + (n_full - 1) * kTile;
+    float gv[kVec], gn[kVec], ring[kEncRing][kVec];
+    load_full(tg + sp.begin, tid, gv);
+#pragma unroll
+    for (int i = 0; i < kEncRing - 1; ++i) load_full(learner_row(a, i < kc ? i : kc - 1, td) + sp.begin, tid, ring[i]);
+    for (int64_t base = sp.begin; base <= last; base += kTile) {
+      const int64_t nbase = base < last ? base + kTile : last;
+      load_full(tg + nbase, tid, gn);
+      for (int i0 = 0; i0 < items; i0 += kEncRing) {
+#pragma unroll
+        for (int u = 0; u < kEncRing; ++u) {
+          const int i = i0 + u;
+          int ip = i + kEncRing - 1;
+          int64_t pb = base;
+          if (ip >= items) {
+            ip -= items;
+            pb = nbase;
+          }
+          load_full(learner_row(a, ip < kc ? ip : kc - 1, td) + pb, tid, ring[(u + kEncRing - 1) % kEncRing]);
+          if (i < kc) {
+            encode_tile<true>(hist + i * kBuckets, st, codes_of(i) + base, gv, ring[u], par[i], tid, kTile);
+          }
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) gv[e] = gn[e];
+    }
+  }
+  const int64_t full_end = sp.begin + n_full * kTile;
+  if (full_end < sp.end) {
+    const int64_t n = sp.end - full_end;
     float gv[kVec];
-    if (full) load_full(tg + base, tid, gv); else load_tail(tg + base, tid, n, gv);
-
+    load_tail(tg + full_end, tid, n, gv);
     for (int k = 0; k < kc; ++k) {
-      const int li = a.learner[a.k_base + k];
-      const int64_t row = (int64_t)li * a.stride + td.loffset + base;
-      const float4 r = a.range[(size_t)li * g.n_tensors_call + rrow];
-      const float lo = r.x, hi = r.y, wd = r.z;
-      const bool degenerate = !(wd >= FLT_MIN);
-      double* hs = hsum + k * kBuckets;
-      uint32_t* hc = hcnt + k * kBuckets;
       float lv[kVec];
-      if (full) load_full(a.theta_L + row, tid, lv); else load_tail(a.theta_L + row, tid, n, lv);
-
-      uint32_t packed[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = 4 * j + c;
-          const float x = gv[e] - lv[e];
-          uint32_t code = 0;
-          if (!degenerate) {
-            code = bucket_of(x, lo, wd);
-            if (full || tail_valid(tid, j, c, n)) {
-              const float xc = fminf(fmaxf(x, lo), hi);
-              atomicAdd(&hs[code], (double)xc);
-              atomicAdd(&hc[code], 1u);
-            }
-          }
-          w |= code << (8 * c);
-        }
-        packed[j] = w;
-      }
-
-      uint8_t* cp = a.codes + row;
-      if (full) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) st[j * 64 + lane] = packed[j];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int j = lane >> 4, r16 = lane & 15;
-        const uint4 v = *reinterpret_cast<const uint4*>(st + j * 64 + 4 * r16);
-        *reinterpret_cast<uint4*>(cp + 4 * (j * kBlock + 64 * wave + 4 * r16)) = v;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (tail_valid(tid, j, c, n)) cp[4 * (j * kBlock + tid) + c] = (uint8_t)(packed[j] >> (8 * c));
-          }
-        }
-      }
+      load_tail(learner_row(a, k, td) + full_end, tid, n, lv);
+      encode_tile<false>(hist + k * kBuckets, st, codes_of(k) + full_end, gv, lv, par[k], tid, n);
     }
   }
 
   __syncthreads();
   const size_t slot = (size_t)(g.slot_base + blockIdx.x);
-  for (int i = tid; i < kc * kBuckets; i += kBlock) {
-    const int k = i >> 8, c = i & (kBuckets - 1);
-    const size_t o = ((slot * a.n_present) + a.k_base + k) * kBuckets + c;
-    a.part_sum[o] = hsum[i];
-    a.part_cnt[o] = hcnt[i];
-  }
+  uint64_t* dst = a.part_hist + (slot * a.n_present + a.k_base) * kBuckets;
+  for (int i = tid; i < kc * kBuckets; i += kBlock) dst[i] = hist[i];
 }
 
 // ---------------------------------------------------------------------------
-// k_codebook: one block of 256 threads per (present learner, tensor); thread c
-// sums bucket c over the tensor's blocks in block order.
+// k_codebook: one block of 1024 threads per (present learner, tensor).  Thread
+// (g, c) sums bucket c over every fourth block partial of the tensor (integer, so
+// the order does not matter), the four groups combine in LDS, then
+//   cb[c] = fl32(lo + wd * (c + Q / (n * 2^s)))
+// with n the bucket count and Q the sum of the element positions q; an empty
+// bucket holds its midpoint fl32(lo + (c + 1/2) wd).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBuckets) void k_codebook(const QuantArgs a, const LaunchGeom g) {
+constexpr int kCodebookGroups = 4;
+
+__global__ __launch_bounds__(kBuckets * kCodebookGroups) void k_codebook(const QuantArgs a, const LaunchGeom g) {
+  __shared__ int64_t sq[kCodebookGroups][kBuckets];
+  __shared__ uint64_t sn[kCodebookGroups][kBuckets];
   const int k = blockIdx.x / g.n_tensors;
   const int t = blockIdx.x - k * g.n_tensors;
-  const int c = threadIdx.x;
+  const int c = threadIdx.x & (kBuckets - 1);
+  const int grp = threadIdx.x >> 8;
   const int li = a.learner[k];
   const size_t row = (size_t)li * g.n_tensors_call + g.t_base + t;
   const float4 r = a.range[row];
+  const int b0 = g.t[t].block_first, b1 = tensor_block_end(g, t);
+  const size_t step = (size_t)a.n_present * kBuckets;
+  const uint64_t* p = a.part_hist + ((size_t)(g.slot_base + b0) * a.n_present + k) * kBuckets + c;
+  int64_t Q = 0;
+  uint64_t N = 0;
+  int b = grp;
+  for (; b + 7 * kCodebookGroups < b1 - b0; b += 8 * kCodebookGroups) {
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(b + u * kCodebookGroups) * step];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t n = v[u] >> kHistCountShift;
+      N += n;
+      Q += (int64_t)(v[u] & ((1ull << kHistCountShift) - 1)) - (int64_t)n * kHistBias;
+    }
+  }
+  for (; b < b1 - b0; b += kCodebookGroups) {
+    const uint64_t v = p[(size_t)b * step];
+    const uint64_t n = v >> kHistCountShift;
+    N += n;
+    Q += (int64_t)(v & ((1ull << kHistCountShift) - 1)) - (int64_t)n * kHistBias;
+  }
+  sq[grp][c] = Q;
+  sn[grp][c] = N;
+  __syncthreads();
+  if (grp != 0) return;
+  for (int u = 1; u < kCodebookGroups; ++u) {
+    Q += sq[u][c];
+    N += sn[u][c];
+  }
   float out;
   if (!(r.z >= FLT_MIN)) {
     out = r.w;
+  } else if (N > 0) {
+    const int s = hist_frac_bits(r.x, r.y, r.z);
+    const double frac = (double)Q / ((double)N * (double)(1ll << s));
+    out = (float)((double)r.x + (double)r.z * ((double)c + frac));
   } else {
-    const int b0 = g.t[t].block_first, b1 = tensor_block_end(g, t);
-    double S = 0.0;
-    uint64_t n = 0;
-    for (int b = b0; b < b1; ++b) {
-      const size_t o = ((size_t)(g.slot_base + b) * a.n_present + k) * kBuckets + c;
-      S += a.part_sum[o];
-      n += a.part_cnt[o];
-    }
-    if (n > 0) {
-      out = (float)(S / (double)n);
-    } else {
-      out = (float)((double)r.x + ((double)c + 0.5) * (double)r.z);
-    }
+    out = (float)((double)r.x + ((double)c + 0.5) * (double)r.z);
   }
   a.codebook[row * kBuckets + c] = out;
 }
@@ -366,6 +586,35 @@ __global__ __launch_bounds__(kBuckets) void k_codebook(const QuantArgs a, const 
 // k_merge: g = sum_i tab_i[code_i] with tab_i[c] = w_hat_i * codebook_i[c] (fp64,
 // in LDS), learners in index order; then the Nesterov step in fp64.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void nesterov16(float (&tv)[kVec], float (&vv)[kVec], const double (&acc)[kVec],
+                                           double lr, double beta) {
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    const double gsum = acc[e];
+    const double bv = beta * (double)vv[e];
+    const double vn = bv + gsum;
+    const double bvn = beta * vn;
+    const double step = gsum + bvn;
+    const double u = lr * step;
+    const double tn = (double)tv[e] - u;
+    tv[e] = (float)tn;
+    vv[e] = (float)vn;
+  }
+}
+
+__device__ __forceinline__ void load_codes_full(const uint8_t* __restrict__ cp, int tid, uint32_t (&cw)[4]) {
+  const uint32_t* q = reinterpret_cast<const uint32_t*>(cp);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) cw[j] = __builtin_nontemporal_load(q + f4_index(tid, j));
+}
+
+// Code words of (learner, tile) items stream through a ring of kMergeRing
+// registers (item i + kMergeRing - 1 is requested while item i is looked up),
+// items per tile padded to a multiple of the ring, requests unconditional.
+// theta and momentum of a tile are requested when the tile starts; they are
+// needed only after every learner has been looked up.
+constexpr int kMergeRing = 4;
+
 __global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const LaunchGeom g) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* tab = reinterpret_cast<double*>(smem);
@@ -384,83 +633,90 @@ __global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const Launc
 
   float* __restrict__ th = a.theta_g + td.offset;
   float* __restrict__ mv = a.momentum + td.offset;
+  auto codes_of = [&](int k) { return a.codes + (int64_t)a.learner[k] * a.stride + td.loffset; };
   const double lr = a.lr, beta = a.beta;
 
-  for (int64_t base = sp.begin; base < sp.end; base += kTile) {
-    const int64_t n = sp.end - base;
-    const bool full = n >= kTile;
-    float tv[kVec], vv[kVec];
-    if (full) {
+  const int64_t n_full = (sp.end - sp.begin) / kTile;
+  if (n_full > 0) {
+    const int items = (kp + kMergeRing - 1) / kMergeRing * kMergeRing;
+    const int64_t last = sp.begin + (n_full - 1) * kTile;
+    uint32_t ring[kMergeRing][4];
+#pragma unroll
+    for (int i = 0; i < kMergeRing - 1; ++i) load_codes_full(codes_of(i < kp ? i : kp - 1) + sp.begin, tid, ring[i]);
+    for (int64_t base = sp.begin; base <= last; base += kTile) {
+      const int64_t nbase = base < last ? base + kTile : last;
+      float tv[kVec], vv[kVec];
       load_full(th + base, tid, tv);
       load_full(mv + base, tid, vv);
-    } else {
-      load_tail(th + base, tid, n, tv);
-      load_tail(mv + base, tid, n, vv);
+      double acc[kVec];
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) acc[e] = 0.0;
+      for (int i0 = 0; i0 < items; i0 += kMergeRing) {
+#pragma unroll
+        for (int u = 0; u < kMergeRing; ++u) {
+          const int i = i0 + u;
+          int ip = i + kMergeRing - 1;
+          int64_t pb = base;
+          if (ip >= items) {
+            ip -= items;
+            pb = nbase;
+          }
+          load_codes_full(codes_of(ip < kp ? ip : kp - 1) + pb, tid, ring[(u + kMergeRing - 1) % kMergeRing]);
+          if (i < kp) {
+            const double* tk = tab + i * kBuckets;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) acc[4 * j + c] += tk[(ring[u][j] >> (8 * c)) & 0xffu];
+            }
+          }
+        }
+      }
+      nesterov16(tv, vv, acc, lr, beta);
+      store_full(th + base, tid, tv);
+      store_full(mv + base, tid, vv);
     }
+  }
+  const int64_t full_end = sp.begin + n_full * kTile;
+  if (full_end < sp.end) {
+    const int64_t n = sp.end - full_end;
+    float tv[kVec], vv[kVec];
+    load_tail(th + full_end, tid, n, tv);
+    load_tail(mv + full_end, tid, n, vv);
     double acc[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc[e] = 0.0;
-
     for (int k = 0; k < kp; ++k) {
-      const uint8_t* cp = a.codes + (int64_t)a.learner[k] * a.stride + td.loffset + base;
-      uint32_t cw[4];
-      if (full) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) cw[j] = *reinterpret_cast<const uint32_t*>(cp + 4 * (j * kBlock + tid));
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t w = 0;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (tail_valid(tid, j, c, n)) w |= (uint32_t)cp[4 * (j * kBlock + tid) + c] << (8 * c);
-          }
-          cw[j] = w;
-        }
-      }
+      const uint8_t* cp = codes_of(k) + full_end;
       const double* tk = tab + k * kBuckets;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[4 * j + c] += tk[(cw[j] >> (8 * c)) & 0xffu];
-      }
-    }
-
-#pragma unroll
-    for (int e = 0; e < kVec; ++e) {
-      const double gsum = acc[e];
-      const double bv = beta * (double)vv[e];
-      const double vn = bv + gsum;
-      const double bvn = beta * vn;
-      const double step = gsum + bvn;
-      const double u = lr * step;
-      const double tn = (double)tv[e] - u;
-      tv[e] = (float)tn;
-      vv[e] = (float)vn;
-    }
-
-    if (full) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        *reinterpret_cast<float4*>(th + base + 4 * (j * kBlock + tid)) =
-            make_float4(tv[4 * j], tv[4 * j + 1], tv[4 * j + 2], tv[4 * j + 3]);
-        *reinterpret_cast<float4*>(mv + base + 4 * (j * kBlock + tid)) =
-            make_float4(vv[4 * j], vv[4 * j + 1], vv[4 * j + 2], vv[4 * j + 3]);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
         for (int c = 0; c < 4; ++c) {
-          if (tail_valid(tid, j, c, n)) {
-            const int64_t e = base + 4 * (j * kBlock + tid) + c;
-            th[e] = tv[4 * j + c];
-            mv[e] = vv[4 * j + c];
-          }
+          if (tail_valid(tid, j, c, n)) acc[4 * j + c] += tk[cp[elem_index(tid, j, c)]];
+        }
+      }
+    }
+    nesterov16(tv, vv, acc, lr, beta);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (tail_valid(tid, j, c, n)) {
+          const int64_t e = full_end + elem_index(tid, j, c);
+          th[e] = tv[4 * j + c];
+          mv[e] = vv[4 * j + c];
         }
       }
     }
   }
+}
+
+template <typename K>
+hipError_t allow_lds(K kernel, size_t lds) {
+  if (lds <= 65536) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
 }
 
 }  // namespace
@@ -468,10 +724,8 @@ __global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const Launc
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
   if (a.k_count <= 4) {
     hipLaunchKernelGGL(k_stats<4>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
-  } else if (a.k_count <= 8) {
-    hipLaunchKernelGGL(k_stats<8>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
   } else {
-    hipLaunchKernelGGL(k_stats<16>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
+    hipLaunchKernelGGL(k_stats<kStatsChunk>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
   }
   return hipGetLastError();
 }
@@ -482,25 +736,27 @@ hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) 
   return hipGetLastError();
 }
 
+size_t encode_lds_bytes(int k_count) {
+  return (size_t)k_count * kHistBytes + (size_t)kWaves * 256 * sizeof(uint32_t) + (size_t)k_count * sizeof(EncodePar);
+}
+
 hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
-  const size_t lds = (size_t)a.k_count * kBuckets * (sizeof(double) + sizeof(uint32_t)) +
-                     (size_t)kWaves * 256 * sizeof(uint32_t);
+  const size_t lds = encode_lds_bytes(a.k_count);
+  hipError_t e = allow_lds(k_encode, lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_encode, dim3(g.n_blocks), dim3(kBlock), lds, s, a, g);
   return hipGetLastError();
 }
 
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
-  hipLaunchKernelGGL(k_codebook, dim3(a.n_present * g.n_tensors), dim3(kBuckets), 0, s, a, g);
+  hipLaunchKernelGGL(k_codebook, dim3(a.n_present * g.n_tensors), dim3(kBuckets * kCodebookGroups), 0, s, a, g);
   return hipGetLastError();
 }
 
 hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) {
   const size_t lds = (size_t)a.n_present * kBuckets * sizeof(double);
-  if (lds > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_merge),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
+  hipError_t e = allow_lds(k_merge, lds);
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_merge, dim3(g.n_blocks), dim3(kBlock), lds, s, a, g);
   return hipGetLastError();
 }

@@ -96,8 +96,8 @@ def test_stages_equal_fused_and_deterministic():
         for i in range(k):
             for (o, lo, n) in inp.tensors:
                 assert torch.equal(a["codes"][i, lo:lo + n], x["codes"][i, lo:lo + n])
-        u = parity.ulp_distance(parity.host(a["codebook"]), parity.host(x["codebook"]))
-        assert u.max() <= 1
+        # integer histograms: the codebook does not depend on the order of the atomics
+        assert torch.equal(a["codebook"], x["codebook"])
 
 
 def test_no_quorum_changes_nothing():

@@ -195,7 +195,7 @@ def draw_delta(cfg: Config, spec: TensorSpec, tensor_sigma: float, gen: torch.Ge
         return torch.where(u < 1e-3, z * 50.0, z)
     if cfg.delta == "laplace":
         u = torch.rand(n, generator=gen, dtype=torch.float32, device=device) - 0.5
-        mag = -torch.log1p(-2.0 * u.abs()).clamp_(max=80.0)
+        mag = torch.neg(torch.log1p(-2.0 * u.abs())).clamp_(max=80.0)  # finite when u = -1/2
         return (torch.sign(u) * mag).mul_(cfg.delta_scale)
     raise ValueError(cfg.delta)
 
