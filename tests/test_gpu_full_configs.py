@@ -1,0 +1,205 @@
+"""GPU parity at the full sizes of every parameter set, in the call shape the
+benchmark times (one quantize-range, one quantize-encode and one merge call over
+all tensors of the call).  The oracle checks sampled tensors one by one: a
+tensor's statistics, codes, codebooks and update depend on that tensor only, so
+each sampled tensor is an exact oracle case (tolerances in tests/parity.py).
+"""
+import numpy as np
+import pytest
+import torch
+
+import diloco_outer_step_amd as dlc
+import oracle
+import workloads
+from tests import parity
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+DEV = "cuda"
+
+
+class TensorView:
+    """One tensor of a call, copied to host, in the form tests/parity.compare takes."""
+
+    def __init__(self, inp, t, theta_before, mom_before):
+        off, loff, n = inp.tensors[t]
+        k = inp.theta_L.shape[0]
+        stride = (n + 63) // 64 * 64
+        self.theta_g = theta_before[off:off + n].clone()
+        self.momentum = mom_before[off:off + n].clone()
+        self.theta_L = torch.zeros((k, stride), dtype=torch.float32, device=inp.theta_L.device)
+        for i in range(k):
+            if inp.present[i]:
+                self.theta_L[i, :n] = inp.theta_L[i, loff:loff + n]
+        self.tensors = [(0, 0, n)]
+        self.weights = inp.weights
+        self.present = inp.present
+        self.src = (t, off, loff, n)
+
+
+def run_call(inp, theta, mom, lr, beta):
+    """The benchmark's three calls on (theta, mom) in place; returns codes, codebook, range."""
+    k, stride = inp.theta_L.shape
+    codes, cb, rng = dlc.outputs_for(k, stride, len(inp.tensors), DEV)
+    ws = dlc.alloc_workspace(k, inp.tensors, DEV)
+    dlc.dlc_quantize_range(theta, inp.theta_L, inp.tensors, rng, ws, present=inp.present)
+    dlc.dlc_quantize_encode(theta, inp.theta_L, inp.tensors, rng, codes, cb, ws, present=inp.present)
+    dlc.dlc_merge_outer_step(theta, mom, codes, cb, inp.weights, inp.tensors, lr, beta)
+    torch.cuda.synchronize()
+    return codes, cb, rng
+
+
+def check_sampled(inp, picks, theta_before, mom_before, theta_after, mom_after, codes, cb, rng, cfg, tag):
+    reports = []
+    for t in picks:
+        view = TensorView(inp, t, theta_before, mom_before)
+        _, off, loff, n = view.src
+        gpu = dict(codes=torch.zeros_like(view.theta_L, dtype=torch.uint8), codebook=cb[:, t:t + 1],
+                   range=rng[:, t:t + 1], theta=theta_after[off:off + n], momentum=mom_after[off:off + n])
+        gpu["codes"][:, :n] = codes[:, loff:loff + n]
+        orc = parity.oracle_step(view, cfg.lr, cfg.beta)
+        rep = parity.compare(gpu, orc, view, pinned=False)
+        reports.append((t, n, rep))
+        print(f"[{tag}] tensor {t} ({n} params): flips {rep['flips']}, range ulp max {rep['range_ulp_max']}, "
+              f"codebook ulp max {rep['cb_ulp_max']}, theta exact {rep['theta_exact']}/{n}", flush=True)
+    return reports
+
+
+def pick_tensors(inp, max_params=20_000_000):
+    """Smallest, median-size and largest-affordable tensors of the call."""
+    sizes = [(n, t) for t, (_, _, n) in enumerate(inp.tensors)]
+    sizes.sort()
+    picks = {sizes[0][1], sizes[len(sizes) // 2][1]}
+    for n, t in reversed(sizes):
+        if n <= max_params:
+            picks.add(t)
+            break
+    return sorted(picks)
+
+
+def fragment_ids(cfg, which):
+    numel = [s.numel for s in cfg.tensors]
+    frag, loads = dlc.dlc_fragment_plan(numel, cfg.n_fragments)
+    order = sorted(range(cfg.n_fragments), key=lambda p: (loads[p], p))
+    p = {"median": order[cfg.n_fragments // 2], "largest": order[-1], "smallest": order[0]}[which]
+    return [t for t, f in enumerate(frag) if f == p], p
+
+
+def test_c1_full():
+    cfg = workloads.config("c1")
+    inp = workloads.fragment_inputs(cfg, [0], DEV)
+    theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+    codes, cb, rng = run_call(inp, theta, mom, cfg.lr, cfg.beta)
+    check_sampled(inp, [0], inp.theta_g, inp.momentum, theta, mom, codes, cb, rng, cfg, "c1")
+
+
+def test_c2_full_cycle_of_24_fragments():
+    """135M set: every one of the 24 fragments merged in turn; sampled tensors from
+    the median fragment and the embedding fragment checked against the oracle."""
+    cfg = workloads.config("c2")
+    ids = list(range(len(cfg.tensors)))
+    inp = workloads.fragment_inputs(cfg, ids, DEV)
+    numel = [s.numel for s in cfg.tensors]
+    frag, loads = dlc.dlc_fragment_plan(numel, 24)
+    theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+    outs = {}
+    for p in range(24):
+        sel = [t for t in ids if frag[t] == p]
+        if not sel:
+            continue
+        sub = workloads.StepInputs(inp.theta_g, inp.momentum, inp.theta_L, [inp.tensors[t] for t in sel],
+                                   inp.weights, inp.present, sel, inp.learner_stride)
+        before = theta.clone()
+        codes, cb, rng = run_call(sub, theta, mom, cfg.lr, cfg.beta)
+        outs[p] = (sub, before, codes, cb, rng)
+    order = sorted(range(24), key=lambda q: (loads[q], q))
+    for p in (order[12], order[-1]):
+        sub, before, codes, cb, rng = outs[p]
+        # every tensor of this fragment was untouched before its own call
+        check_sampled(sub, pick_tensors(sub), before, torch.zeros_like(mom), theta, mom, codes, cb, rng, cfg,
+                      f"c2 fragment {p}")
+
+
+def test_c3_ten_steps_with_momentum():
+    """1B set, K=8, Dirichlet weights: 10 consecutive outer steps, fresh learners
+    each step from the current theta, momentum carried; sampled tensors checked
+    against the oracle at every step (inputs of step s are the GPU's state after
+    step s - 1)."""
+    cfg = workloads.config("c3")
+    ids = list(range(len(cfg.tensors)))
+    theta, mom, offs = workloads.build_global(cfg, ids, DEV)
+    sig = workloads.tensor_sigmas(cfg, len(ids))
+    w = workloads.base_weights(cfg)
+    picks = None
+    for step in range(10):
+        theta_L, loffs, stride = workloads.build_learners(cfg, ids, theta, offs, DEV, step=step, sigmas=sig)
+        tens = [(o, lo, cfg.tensors[t].numel) for o, lo, t in zip(offs, loffs, ids)]
+        inp = workloads.StepInputs(theta, mom, theta_L, tens, w, [1] * cfg.n_learners, ids, stride)
+        before_t, before_m = theta.clone(), mom.clone()
+        codes, cb, rng = run_call(inp, theta, mom, cfg.lr, cfg.beta)
+        if picks is None:
+            picks = pick_tensors(inp, 12_000_000)
+        if step in (0, 1, 9):
+            check_sampled(inp, picks, before_t, before_m, theta, mom, codes, cb, rng, cfg, f"c3 step {step}")
+        del theta_L, codes
+        torch.cuda.empty_cache()
+    assert torch.isfinite(theta).all() and torch.isfinite(mom).all()
+
+
+@pytest.mark.parametrize("which", ["median", "largest"])
+def test_c4_fragment(which):
+    """10B set, K=14, outliers: one fragment with its 14 replicas resident."""
+    cfg = workloads.config("c4")
+    ids, p = fragment_ids(cfg, which)
+    inp = workloads.fragment_inputs(cfg, ids, DEV, fragment=p)
+    theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+    codes, cb, rng = run_call(inp, theta, mom, cfg.lr, cfg.beta)
+    picks = pick_tensors(inp, 17_000_000) if which == "median" else []
+    if which == "largest":
+        # the 525M embedding / LM head: check the call's codes and state via invariants
+        n = inp.tensors[0][2]
+        assert torch.isfinite(theta[:n]).all()
+        counts = torch.bincount(codes[0, :n].long(), minlength=256)
+        assert int(counts.sum()) == n
+    check_sampled(inp, picks, inp.theta_g, inp.momentum, theta, mom, codes, cb, rng, cfg, f"c4 {which}")
+
+
+def test_c5_k1_whole_set():
+    """3000-tensor edge mix, K=1, weight 1, one call over every tensor: constant
+    tensors, 4096-vectors, 1024^2 and 4096x11008 matrices."""
+    cfg = workloads.config("c5k1")
+    ids = list(range(len(cfg.tensors)))
+    inp = workloads.fragment_inputs(cfg, ids, DEV)
+    theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+    codes, cb, rng = run_call(inp, theta, mom, cfg.lr, cfg.beta)
+    picks = [0, 1999, 2000, 2899, 2900, 2990, 2991, 2999]
+    check_sampled(inp, picks, inp.theta_g, inp.momentum, theta, mom, codes, cb, rng, cfg, "c5 k1")
+    # K = 1, w = 1: g = cb[code] exactly (lr, beta as configured)
+    for t in (2990, 2995):
+        off, loff, n = inp.tensors[t]
+        assert float(rng[0, t, 2]) == 0.0  # zero-variance tensor
+        assert torch.all(codes[0, loff:loff + n] == 0)
+
+
+def test_c5_k16_fragment_with_absent_learners():
+    """Edge mix, K=16: a 347-tensor fragment where each learner is absent with
+    probability 1/4 (weight 0, never read)."""
+    cfg = workloads.config("c5k16")
+    numel = [s.numel for s in cfg.tensors]
+    frag, loads = dlc.dlc_fragment_plan(numel, 24)
+    counts = [sum(1 for f in frag if f == p) for p in range(24)]
+    p = max(range(24), key=lambda q: (counts[q], -q))
+    ids = [t for t, f in enumerate(frag) if f == p]
+    inp = workloads.fragment_inputs(cfg, ids, DEV, fragment=p)
+    assert 0 < sum(inp.present) < 16
+    # absent rows are poisoned: they must never be read
+    for i, pr in enumerate(inp.present):
+        if not pr:
+            inp.theta_L[i].fill_(float("nan"))
+    theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+    codes, cb, rng = run_call(inp, theta, mom, cfg.lr, cfg.beta)
+    assert torch.isfinite(theta).all()
+    picks = pick_tensors(inp)
+    const = [j for j, t in enumerate(ids) if cfg.tensors[t].kind == "const"]
+    check_sampled(inp, sorted(set(picks + const[:2])), inp.theta_g, inp.momentum, theta, mom, codes, cb, rng,
+                  cfg, f"c5 k16 fragment {p}")
