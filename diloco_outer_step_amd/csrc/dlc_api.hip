@@ -32,6 +32,9 @@ int32_t ok() {
 // a 256-CU part, so that the tensor-aligned partition stays balanced.
 constexpr int64_t kTargetBlocks = 2048;
 
+constexpr int64_t kMaxTensorNumel = (int64_t(1) << 32) - 1;
+constexpr int64_t kMaxOffset = (int64_t(1) << 38) - DLC_ALIGN_ELEMS;
+
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
 
 struct Partition {
@@ -60,9 +63,9 @@ Partition make_partition(const dlc_tensor* t, int32_t n, int64_t max_tiles) {
     int64_t blocks = 0;
     for (int32_t i = 0; i < g.n_tensors; ++i) {
       const dlc_tensor& d = t[s + i];
-      g.t[i].offset = d.offset;
-      g.t[i].loffset = d.loffset;
-      g.t[i].numel = d.numel;
+      g.t[i].off64 = (uint32_t)(d.offset / DLC_ALIGN_ELEMS);
+      g.t[i].loff64 = (uint32_t)(d.loffset / DLC_ALIGN_ELEMS);
+      g.t[i].count = (uint32_t)d.numel;
       g.t[i].block_first = (int32_t)blocks;
       const int64_t tiles = (d.numel + dlc::kTile - 1) / dlc::kTile;
       blocks += (tiles + tpb - 1) / tpb;
@@ -98,7 +101,10 @@ int32_t check_tensors(const dlc_tensor* t, int32_t n, int64_t learner_stride, bo
     return fail(DLC_ERR_ALIGNMENT, "learner_stride must be a positive multiple of 64 elements");
   for (int32_t i = 0; i < n; ++i) {
     const dlc_tensor& d = t[i];
-    if (d.numel < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "tensor " + std::to_string(i) + ": numel must be >= 1");
+    if (d.numel < 1 || d.numel > kMaxTensorNumel)
+      return fail(DLC_ERR_INVALID_ARGUMENT, "tensor " + std::to_string(i) + ": numel must be in [1, 2^32 - 1]");
+    if (d.offset > kMaxOffset || d.loffset > kMaxOffset)
+      return fail(DLC_ERR_INVALID_ARGUMENT, "tensor " + std::to_string(i) + ": offset beyond 2^38 elements");
     if (d.offset < 0 || d.loffset < 0)
       return fail(DLC_ERR_INVALID_ARGUMENT, "tensor " + std::to_string(i) + ": negative offset");
     if (d.offset % DLC_ALIGN_ELEMS != 0 || d.loffset % DLC_ALIGN_ELEMS != 0)

@@ -18,7 +18,7 @@ namespace dlc {
 
 constexpr int kBuckets = 256;
 constexpr int kMaxLearners = 64;
-constexpr int kMaxTensorsPerLaunch = 64;
+constexpr int kMaxTensorsPerLaunch = 160;
 constexpr int kVec = 16;                  // elements per thread per tile (4 x float4)
 constexpr int kBlock = 256;               // threads per block
 constexpr int kTile = kBlock * kVec;      // elements per tile
@@ -34,12 +34,16 @@ constexpr int kHistBias = 1 << 13;
 constexpr int kHistCountShift = 44;
 constexpr int kStatsChunk = 8;            // learners per statistics launch (register accumulators)
 
+// 16 bytes per tensor so that up to kMaxTensorsPerLaunch descriptors fit in the
+// kernel arguments: offsets in units of 64 elements, numel below 2^32.
 struct TensorDesc {
-  int64_t offset;       // into theta_global / momentum
-  int64_t loffset;      // into each learner row
-  int64_t numel;
+  uint32_t off64;       // offset into theta_global / momentum, in units of 64 elements
+  uint32_t loff64;      // offset into each learner row, in units of 64 elements
+  uint32_t count;       // number of elements
   int32_t block_first;  // first block of this tensor within the launch
-  int32_t pad;
+  __host__ __device__ int64_t offset() const { return (int64_t)off64 * 64; }
+  __host__ __device__ int64_t loffset() const { return (int64_t)loff64 * 64; }
+  __host__ __device__ int64_t numel() const { return (int64_t)count; }
 };
 
 struct LaunchGeom {

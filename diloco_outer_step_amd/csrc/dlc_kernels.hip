@@ -57,7 +57,7 @@ __device__ __forceinline__ Span block_span(const LaunchGeom& g) {
   const int64_t per_block = (int64_t)g.tiles_per_block * kTile;
   s.begin = (int64_t)(b - g.t[lo].block_first) * per_block;
   const int64_t e = s.begin + per_block;
-  s.end = e < g.t[lo].numel ? e : g.t[lo].numel;
+  s.end = e < g.t[lo].numel() ? e : g.t[lo].numel();
   return s;
 }
 
@@ -122,7 +122,7 @@ __device__ __forceinline__ T wave_sum(T v) {
 }
 
 __device__ __forceinline__ const float* learner_row(const QuantArgs& a, int k, const TensorDesc& td) {
-  return a.theta_L + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset;
+  return a.theta_L + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset();
 }
 
 // ---------------------------------------------------------------------------
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
   const int tid = threadIdx.x;
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
-  const float* __restrict__ tg = a.theta_g + td.offset;
+  const float* __restrict__ tg = a.theta_g + td.offset();
   const int kc = a.k_count;
 
   float shift[KC];  // Delta at element 0: an fp32 value, widened where used
@@ -275,10 +275,10 @@ __global__ __launch_bounds__(64) void k_range(const QuantArgs a, const LaunchGeo
     S2 += v.y;
   }
   const int li = a.learner[k];
-  const float g0 = a.theta_g[td.offset];
-  const float l0 = a.theta_L[(int64_t)li * a.stride + td.loffset];
+  const float g0 = a.theta_g[td.offset()];
+  const float l0 = a.theta_L[(int64_t)li * a.stride + td.loffset()];
   const double shift = (double)(g0 - l0);
-  const double n = (double)td.numel;
+  const double n = (double)td.numel();
   const double m1 = S1 / n;
   const double mu = shift + m1;
   double var = S2 / n - m1 * m1;
@@ -463,10 +463,10 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
   if (tid < kc) par[tid] = make_encode_par(a.range[(size_t)a.learner[a.k_base + tid] * g.n_tensors_call + rrow]);
   __syncthreads();
 
-  const float* __restrict__ tg = a.theta_g + td.offset;
+  const float* __restrict__ tg = a.theta_g + td.offset();
   uint32_t* st = stage + wave * 256;
   auto codes_of = [&](int k) {
-    return a.codes + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset;
+    return a.codes + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset();
   };
 
   const int64_t n_full = (sp.end - sp.begin) / kTile;
@@ -631,9 +631,9 @@ __global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const Launc
   }
   __syncthreads();
 
-  float* __restrict__ th = a.theta_g + td.offset;
-  float* __restrict__ mv = a.momentum + td.offset;
-  auto codes_of = [&](int k) { return a.codes + (int64_t)a.learner[k] * a.stride + td.loffset; };
+  float* __restrict__ th = a.theta_g + td.offset();
+  float* __restrict__ mv = a.momentum + td.offset();
+  auto codes_of = [&](int k) { return a.codes + (int64_t)a.learner[k] * a.stride + td.loffset(); };
   const double lr = a.lr, beta = a.beta;
 
   const int64_t n_full = (sp.end - sp.begin) / kTile;

@@ -38,9 +38,10 @@
  *     indexed [learner][t] with the call's tensor index t in 0..n_tensors-1 and the
  *     learner's own index i in 0..n_learners-1.
  *   - Alignment: device base pointers 256-byte aligned; offset, loffset and
- *     learner_stride multiples of 64 elements; numel >= 1 (any value; tails are
- *     handled on the device).  Tensor ranges must not overlap, in theta_global nor
- *     within a learner row.
+ *     learner_stride multiples of 64 elements; 1 <= numel <= 2^32 - 1 (any value
+ *     in that range; tails are handled on the device); offsets below 2^38
+ *     elements.  Tensor ranges must not overlap, in theta_global nor within a
+ *     learner row.
  *   - Limits: 1 <= n_learners <= DLC_MAX_LEARNERS; n_tensors >= 1.
  */
 #ifndef DLC_H
@@ -117,11 +118,15 @@ int32_t dlc_quantize_range(const float* theta_global, const float* theta_learner
 
 /*
  * dlc_quantize_encode -- stage B of quantization (INTELLECT-1 notes, section 4.1
- * steps 2-4).  Given range[i][t] = {lo, hi, wd, mean}:
+ * steps 2-4).  Given range[i][t] = {lo, hi, wd, mean} with lo <= hi:
  *   code  = clip(floor(fl32(fl32(Delta - lo) / wd)), 0, 255)   (IEEE fp32, RNE)
  *   x_c   = min(max(Delta, lo), hi)
- *   codebook[i][t][c] = fl32(sum of x_c in bucket c / count)   (sums in fp64)
- *                       or the midpoint fl32(lo + (c + 1/2) wd) for an empty bucket
+ *   codebook[i][t][c] = fl32(mean of x_c over bucket c), or the midpoint
+ *                       fl32(lo + (c + 1/2) wd) for an empty bucket.
+ *   The bucket means come from exact integer sums of every element's position
+ *   inside its bucket, each rounded to units of wd * 2^-26, so an entry is within
+ *   wd * 2^-27 of the exact mean before its fp32 rounding (and independent of the
+ *   order in which elements are accumulated).
  *   If wd is not a normal fp32 (zero variance), every code is 0 and every
  *   codebook entry is `mean`.
  *   codes     device uint8 [n_learners][learner_stride], written at the tensors'
@@ -136,7 +141,8 @@ int32_t dlc_quantize_encode(const float* theta_global, const float* theta_learne
 
 /*
  * dlc_quantize -- dlc_quantize_range followed by dlc_quantize_encode.  With
- * DLC_RANGE_GIVEN in `flags`, `range` is an input and only the encode stage runs.
+ * DLC_RANGE_GIVEN in `flags`, `range` is an input (lo <= hi) and only the encode
+ * stage runs.
  */
 int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
                      int64_t learner_stride, int32_t n_learners, const uint8_t* present,

@@ -113,6 +113,8 @@ def merge(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), lr=0.7, be
     (lambda: quantize(stride=4000), dlc.DLC_ERR_ALIGNMENT),
     (lambda: quantize(spec=((0, 0, 0),)), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: quantize(spec=((0, 0, 4097),)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(spec=((0, 0, 1 << 32),), stride=1 << 33), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(spec=((1 << 38, 0, 64),)), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: quantize(spec=((0, 0, 128), (64, 128, 64)), stride=4096), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: quantize(spec=((0, 0, 128), (128, 64, 64)), stride=4096), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: quantize(present=[0, 0]), dlc.DLC_ERR_NO_QUORUM),
