@@ -143,17 +143,19 @@ __device__ __forceinline__ void stats_accumulate(const float (&gv)[kVec], const 
   }
 }
 
-// Learner tiles stream through a ring of kStatsRing register buffers: the tile of
-// learner item i + kStatsRing - 1 is requested while item i is accumulated.  KC is
-// a multiple of the ring size so ring slots are compile-time constants across
-// tiles; items beyond k_count re-request a valid tile and are not accumulated.
-// Every request is unconditional (clamped addresses), so the wait counts the
-// compiler derives stay exact and never drain the ring.
-constexpr int kStatsRing = 4;
+// Tiles stream through a ring of kStatsRing register buffers.  A tile is KC + 1
+// items: theta_g first, then learners 0..KC-1; item i + kStatsRing - 1 is
+// requested while item i is accumulated.  KC + 1 is a multiple of the ring size,
+// so ring slots are compile-time constants across tiles.  A learner item beyond
+// k_count re-requests the tile's theta_g (just read, so normally still in L2)
+// and is not accumulated.  Every request is the same unconditional load with a
+// selected, clamped address, so the compiler's wait counts stay exact.
+constexpr int kStatsRing = 3;
 
 template <int KC>
 __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const LaunchGeom g) {
-  static_assert(KC % kStatsRing == 0, "KC must be a multiple of the ring size");
+  static_assert((KC + 1) % kStatsRing == 0, "KC + 1 must be a multiple of the ring size");
+  constexpr int kItems = KC + 1;
   const int tid = threadIdx.x;
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
@@ -174,23 +176,30 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
   const int64_t n_full = (sp.end - sp.begin) / kTile;
   if (n_full > 0) {
     const int64_t last = sp.begin + (n_full - 1) * kTile;
-    float gv[kVec], gn[kVec], ring[kStatsRing][kVec];
-    load_full(tg + sp.begin, tid, gv);
+    auto request = [&](int item, int64_t base, float (&dst)[kVec]) {
+      const float* src = (item == 0 || item > kc) ? tg : learner_row(a, item - 1, td);
+      load_full(src + base, tid, dst);
+    };
+    float gv[kVec], ring[kStatsRing][kVec];
 #pragma unroll
-    for (int i = 0; i < kStatsRing - 1; ++i) load_full(learner_row(a, i < kc ? i : kc - 1, td) + sp.begin, tid, ring[i]);
+    for (int i = 0; i < kStatsRing - 1; ++i) request(i, sp.begin, ring[i]);
     for (int64_t base = sp.begin; base <= last; base += kTile) {
       const int64_t nbase = base < last ? base + kTile : last;
-      load_full(tg + nbase, tid, gn);
 #pragma unroll
-      for (int k = 0; k < KC; ++k) {
-        const int ip = k + kStatsRing - 1;
-        const int kl = ip < KC ? ip : ip - KC;
-        const int64_t pb = ip < KC ? base : nbase;
-        load_full(learner_row(a, kl < kc ? kl : kc - 1, td) + pb, tid, ring[ip % kStatsRing]);
-        if (k < kc) stats_accumulate(gv, ring[k % kStatsRing], (double)shift[k], s1[k], s2[k]);
+      for (int i = 0; i < kItems; ++i) {
+        const int ip = i + kStatsRing - 1;
+        if (ip < kItems) {
+          request(ip, base, ring[ip % kStatsRing]);
+        } else {
+          request(ip - kItems, nbase, ring[ip % kStatsRing]);
+        }
+        if (i == 0) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) gv[e] = ring[0][e];
+        } else if (i - 1 < kc) {
+          stats_accumulate(gv, ring[i % kStatsRing], (double)shift[i - 1], s1[i - 1], s2[i - 1]);
+        }
       }
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) gv[e] = gn[e];
     }
   }
   const int64_t full_end = sp.begin + n_full * kTile;
@@ -440,12 +449,13 @@ __device__ __forceinline__ void encode_tile(uint64_t* __restrict__ hist, uint32_
   }
 }
 
-// Learner tiles stream through a ring of kEncRing register buffers (request
-// item i + kEncRing - 1 while encoding item i).  Items per tile are padded to a
-// multiple of the ring so slots are compile-time constants; padded items request
-// a valid tile again and encode nothing.  Requests are unconditional so that the
-// compiler's wait counts stay exact.  Per-learner {lo, hi, wd, 1/wd} are staged
-// in LDS once per block.
+// Items stream through a ring of kEncRing register buffers.  The items of a
+// block are its full tiles in order, each tile being theta_g followed by the
+// k_count learners; item p + kEncRing - 1 is requested while item p is
+// processed, across tile boundaries, so no item is ever padded or read twice
+// (except up to kEncRing - 1 repeated requests at the very end of the block).
+// Per-learner {lo, hi, wd, 1/wd, fixed-point scale} are staged in LDS once per
+// block.
 constexpr int kEncRing = 3;
 
 __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const LaunchGeom g) {
@@ -471,33 +481,43 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
 
   const int64_t n_full = (sp.end - sp.begin) / kTile;
   if (n_full > 0) {
-    const int items = (kc + kEncRing - 1) / kEncRing * kEncRing;
+    const int items_per_tile = kc + 1;
+    const int64_t total = n_full * items_per_tile;
     const int64_t last = sp.begin + (n_full - 1) * kTile;
-    float gv[kVec], gn[kVec], ring[kEncRing][kVec];
-    load_full(tg + sp.begin, tid, gv);
+    // request cursor (tile base, item) runs kEncRing - 1 items ahead of the work cursor
+    int64_t rb = sp.begin;
+    int ri = 0;
+    auto request = [&](float (&dst)[kVec]) {
+      const float* src = ri == 0 ? tg + rb : learner_row(a, ri - 1, td) + rb;
+      load_full(src, tid, dst);
+      if (++ri == items_per_tile) {
+        ri = 0;
+        rb = rb < last ? rb + kTile : last;  // past the end: repeat the last tile
+      }
+    };
+    float gv[kVec], ring[kEncRing][kVec];
 #pragma unroll
-    for (int i = 0; i < kEncRing - 1; ++i) load_full(learner_row(a, i < kc ? i : kc - 1, td) + sp.begin, tid, ring[i]);
-    for (int64_t base = sp.begin; base <= last; base += kTile) {
-      const int64_t nbase = base < last ? base + kTile : last;
-      load_full(tg + nbase, tid, gn);
-      for (int i0 = 0; i0 < items; i0 += kEncRing) {
+    for (int i = 0; i < kEncRing - 1; ++i) request(ring[i]);
+    int64_t wb = sp.begin;
+    int wi = 0;
+    for (int64_t p0 = 0; p0 < total; p0 += kEncRing) {
 #pragma unroll
-        for (int u = 0; u < kEncRing; ++u) {
-          const int i = i0 + u;
-          int ip = i + kEncRing - 1;
-          int64_t pb = base;
-          if (ip >= items) {
-            ip -= items;
-            pb = nbase;
+      for (int u = 0; u < kEncRing; ++u) {
+        if (p0 + u < total) {
+          request(ring[(u + kEncRing - 1) % kEncRing]);
+          if (wi == 0) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) gv[e] = ring[u][e];
+          } else {
+            const int k = wi - 1;
+            encode_tile<true>(hist + k * kBuckets, st, codes_of(k) + wb, gv, ring[u], par[k], tid, kTile);
           }
-          load_full(learner_row(a, ip < kc ? ip : kc - 1, td) + pb, tid, ring[(u + kEncRing - 1) % kEncRing]);
-          if (i < kc) {
-            encode_tile<true>(hist + i * kBuckets, st, codes_of(i) + base, gv, ring[u], par[i], tid, kTile);
+          if (++wi == items_per_tile) {
+            wi = 0;
+            wb += kTile;
           }
         }
       }
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) gv[e] = gn[e];
     }
   }
   const int64_t full_end = sp.begin + n_full * kTile;
@@ -722,8 +742,10 @@ hipError_t allow_lds(K kernel, size_t lds) {
 }  // namespace
 
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
-  if (a.k_count <= 4) {
-    hipLaunchKernelGGL(k_stats<4>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
+  if (a.k_count <= 2) {
+    hipLaunchKernelGGL(k_stats<2>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
+  } else if (a.k_count <= 5) {
+    hipLaunchKernelGGL(k_stats<5>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
   } else {
     hipLaunchKernelGGL(k_stats<kStatsChunk>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
   }
