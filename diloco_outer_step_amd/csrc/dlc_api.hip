@@ -176,7 +176,7 @@ int32_t hip_fail(hipError_t e, const char* what) {
 
 int32_t run_range(Common& c) {
   for (const dlc::LaunchGeom& g : c.part_stats.launches) {
-    // Learners in balanced chunks of at most kStatsChunk (e.g. 14 -> 7 + 7).
+    // Learners in balanced chunks of at most kStatsChunk (e.g. 16 -> 8 + 8).
     const int32_t n_chunks = (c.args.n_present + dlc::kStatsChunk - 1) / dlc::kStatsChunk;
     for (int32_t ci = 0, k0 = 0; ci < n_chunks; ++ci) {
       const int32_t kc = (c.args.n_present - k0) / (n_chunks - ci);

@@ -32,7 +32,7 @@ constexpr int kMaxEncodeTiles = 32;
 constexpr int kHistFracBits = 26;
 constexpr int kHistBias = 1 << 13;
 constexpr int kHistCountShift = 44;
-constexpr int kStatsChunk = 8;            // learners per statistics launch (register accumulators)
+constexpr int kStatsChunk = 14;           // learners per statistics launch (register accumulators)
 
 // 16 bytes per tensor so that up to kMaxTensorsPerLaunch descriptors fit in the
 // kernel arguments: offsets in units of 64 elements, numel below 2^32.

@@ -85,6 +85,27 @@ __device__ __forceinline__ void load_full(const float* __restrict__ p, int tid, 
   }
 }
 
+// 16 floats of a full tile through a buffer descriptor covering just that tile
+// (non-temporal).  A descriptor with zero records makes every load return zeros
+// without touching memory: a "null" request that still counts as a memory
+// instruction, so ring slots without data keep the wait counts static.
+constexpr int kBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const float* p, bool valid) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p), (short)0, valid ? kTile * 4 : 0, kBufferWord3);
+}
+
+__device__ __forceinline__ void load_tile_rsrc(__amdgpu_buffer_rsrc_t r, int tid, float (&v)[kVec]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const vf4 x = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(r, f4_index(tid, j) * 16, 0, 2));
+    v[4 * j + 0] = x.x;
+    v[4 * j + 1] = x.y;
+    v[4 * j + 2] = x.z;
+    v[4 * j + 3] = x.w;
+  }
+}
+
 __device__ __forceinline__ int64_t elem_index(int tid, int j, int c) { return 4 * (int64_t)f4_index(tid, j) + c; }
 
 __device__ __forceinline__ bool tail_valid(int tid, int j, int c, int64_t n) { return elem_index(tid, j, c) < n; }
@@ -147,9 +168,9 @@ __device__ __forceinline__ void stats_accumulate(const float (&gv)[kVec], const 
 // items: theta_g first, then learners 0..KC-1; item i + kStatsRing - 1 is
 // requested while item i is accumulated.  KC + 1 is a multiple of the ring size,
 // so ring slots are compile-time constants across tiles.  A learner item beyond
-// k_count re-requests the tile's theta_g (just read, so normally still in L2)
-// and is not accumulated.  Every request is the same unconditional load with a
-// selected, clamped address, so the compiler's wait counts stay exact.
+// k_count is a null request (zero-record buffer descriptor: no memory traffic)
+// and is not accumulated.  Every request is the same unconditional load through
+// a selected descriptor, so the compiler's wait counts stay exact.
 constexpr int kStatsRing = 3;
 
 template <int KC>
@@ -177,8 +198,9 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
   if (n_full > 0) {
     const int64_t last = sp.begin + (n_full - 1) * kTile;
     auto request = [&](int item, int64_t base, float (&dst)[kVec]) {
-      const float* src = (item == 0 || item > kc) ? tg : learner_row(a, item - 1, td);
-      load_full(src + base, tid, dst);
+      const bool real = item <= kc;
+      const float* src = (item == 0 || !real) ? tg : learner_row(a, item - 1, td);
+      load_tile_rsrc(tile_rsrc(src + base, real), tid, dst);
     };
     float gv[kVec], ring[kStatsRing][kVec];
 #pragma unroll
@@ -622,15 +644,19 @@ __device__ __forceinline__ void nesterov16(float (&tv)[kVec], float (&vv)[kVec],
   }
 }
 
-__device__ __forceinline__ void load_codes_full(const uint8_t* __restrict__ cp, int tid, uint32_t (&cw)[4]) {
-  const uint32_t* q = reinterpret_cast<const uint32_t*>(cp);
+// Code words of one (learner, tile) item: 4 dwords per lane through a buffer
+// descriptor covering the tile's 4096 codes (zero records = null request).
+__device__ __forceinline__ void load_codes_rsrc(const uint8_t* cp, bool valid, int tid, uint32_t (&cw)[4]) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(cp), (short)0, valid ? kTile : 0, kBufferWord3);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) cw[j] = __builtin_nontemporal_load(q + f4_index(tid, j));
+  for (int j = 0; j < 4; ++j) cw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, f4_index(tid, j) * 4, 0, 2);
 }
 
 // Code words of (learner, tile) items stream through a ring of kMergeRing
 // registers (item i + kMergeRing - 1 is requested while item i is looked up),
-// items per tile padded to a multiple of the ring, requests unconditional.
+// items per tile padded to a multiple of the ring with null requests, every
+// request unconditional.
 // theta and momentum of a tile are requested when the tile starts; they are
 // needed only after every learner has been looked up.
 constexpr int kMergeRing = 4;
@@ -662,7 +688,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const Launc
     const int64_t last = sp.begin + (n_full - 1) * kTile;
     uint32_t ring[kMergeRing][4];
 #pragma unroll
-    for (int i = 0; i < kMergeRing - 1; ++i) load_codes_full(codes_of(i < kp ? i : kp - 1) + sp.begin, tid, ring[i]);
+    for (int i = 0; i < kMergeRing - 1; ++i) load_codes_rsrc(codes_of(i < kp ? i : kp - 1) + sp.begin, i < kp, tid, ring[i]);
     for (int64_t base = sp.begin; base <= last; base += kTile) {
       const int64_t nbase = base < last ? base + kTile : last;
       float tv[kVec], vv[kVec];
@@ -681,7 +707,7 @@ __global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const Launc
             ip -= items;
             pb = nbase;
           }
-          load_codes_full(codes_of(ip < kp ? ip : kp - 1) + pb, tid, ring[(u + kMergeRing - 1) % kMergeRing]);
+          load_codes_rsrc(codes_of(ip < kp ? ip : kp - 1) + pb, ip < kp, tid, ring[(u + kMergeRing - 1) % kMergeRing]);
           if (i < kp) {
             const double* tk = tab + i * kBuckets;
 #pragma unroll
@@ -742,12 +768,17 @@ hipError_t allow_lds(K kernel, size_t lds) {
 }  // namespace
 
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
+  const dim3 grid(g.n_blocks), block(kBlock);
   if (a.k_count <= 2) {
-    hipLaunchKernelGGL(k_stats<2>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
+    hipLaunchKernelGGL(k_stats<2>, grid, block, 0, s, a, g);
   } else if (a.k_count <= 5) {
-    hipLaunchKernelGGL(k_stats<5>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
+    hipLaunchKernelGGL(k_stats<5>, grid, block, 0, s, a, g);
+  } else if (a.k_count <= 8) {
+    hipLaunchKernelGGL(k_stats<8>, grid, block, 0, s, a, g);
+  } else if (a.k_count <= 11) {
+    hipLaunchKernelGGL(k_stats<11>, grid, block, 0, s, a, g);
   } else {
-    hipLaunchKernelGGL(k_stats<kStatsChunk>, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
+    hipLaunchKernelGGL(k_stats<14>, grid, block, 0, s, a, g);
   }
   return hipGetLastError();
 }
