@@ -35,7 +35,7 @@ typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = kBlock / 64;
-constexpr int kHistBytes = kBuckets * 8;  // per learner: 256 packed 64-bit bucket accumulators
+constexpr int kHistBytes = kBuckets * 8;  // one copy of a learner's 256 packed 64-bit bucket accumulators
 
 struct Span {
   int t;          // tensor index within the launch
@@ -393,7 +393,7 @@ __device__ __forceinline__ EncodePar make_encode_par(float4 r) {
   return p;
 }
 
-template <bool FULL>
+template <bool FULL, int R>
 __device__ __forceinline__ void encode_tile(uint64_t* __restrict__ hist, uint32_t* __restrict__ st,
                                             uint8_t* __restrict__ cp, const float (&gv)[kVec],
                                             const float (&lv)[kVec], const EncodePar& par_lds, int tid,
@@ -441,7 +441,7 @@ __device__ __forceinline__ void encode_tile(uint64_t* __restrict__ hist, uint32_
           const double off = __fma_rn((double)cf, neg_two_s, neg_lo_scale);
           const int32_t q = (int32_t)__builtin_rint(__fma_rn(xc, scale, off));
           const uint64_t add = ((uint64_t)1 << kHistCountShift) + (uint32_t)(q + kHistBias);
-          atomicAdd(reinterpret_cast<unsigned long long*>(hist + code), (unsigned long long)add);
+          atomicAdd(reinterpret_cast<unsigned long long*>(hist + (code * R + (tid & (R - 1)))), (unsigned long long)add);
         }
         w |= code << (8 * c);
       }
@@ -480,18 +480,19 @@ __device__ __forceinline__ void encode_tile(uint64_t* __restrict__ hist, uint32_
 // block.
 constexpr int kEncRing = 3;
 
+template <int R>
 __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const LaunchGeom g) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int kc = a.k_count;
   uint64_t* hist = reinterpret_cast<uint64_t*>(smem);
-  uint32_t* stage = reinterpret_cast<uint32_t*>(smem + kc * kHistBytes);
+  uint32_t* stage = reinterpret_cast<uint32_t*>(smem + kc * R * kHistBytes);
   EncodePar* par = reinterpret_cast<EncodePar*>(stage + kWaves * 256);
   const int tid = threadIdx.x, wave = tid >> 6;
 
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
   const size_t rrow = (size_t)g.t_base + sp.t;
-  for (int i = tid; i < kc * (kHistBytes / 8); i += kBlock) reinterpret_cast<uint64_t*>(smem)[i] = 0;
+  for (int i = tid; i < kc * R * kBuckets; i += kBlock) hist[i] = 0;
   if (tid < kc) par[tid] = make_encode_par(a.range[(size_t)a.learner[a.k_base + tid] * g.n_tensors_call + rrow]);
   __syncthreads();
 
@@ -532,7 +533,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
             for (int e = 0; e < kVec; ++e) gv[e] = ring[u][e];
           } else {
             const int k = wi - 1;
-            encode_tile<true>(hist + k * kBuckets, st, codes_of(k) + wb, gv, ring[u], par[k], tid, kTile);
+            encode_tile<true, R>(hist + k * R * kBuckets, st, codes_of(k) + wb, gv, ring[u], par[k], tid, kTile);
           }
           if (++wi == items_per_tile) {
             wi = 0;
@@ -550,14 +551,19 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
     for (int k = 0; k < kc; ++k) {
       float lv[kVec];
       load_tail(learner_row(a, k, td) + full_end, tid, n, lv);
-      encode_tile<false>(hist + k * kBuckets, st, codes_of(k) + full_end, gv, lv, par[k], tid, n);
+      encode_tile<false, R>(hist + k * R * kBuckets, st, codes_of(k) + full_end, gv, lv, par[k], tid, n);
     }
   }
 
   __syncthreads();
   const size_t slot = (size_t)(g.slot_base + blockIdx.x);
   uint64_t* dst = a.part_hist + (slot * a.n_present + a.k_base) * kBuckets;
-  for (int i = tid; i < kc * kBuckets; i += kBlock) dst[i] = hist[i];
+  for (int i = tid; i < kc * kBuckets; i += kBlock) {
+    uint64_t v = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) v += hist[i * R + r];
+    dst[i] = v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -789,16 +795,32 @@ hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) 
   return hipGetLastError();
 }
 
-size_t encode_lds_bytes(int k_count) {
-  return (size_t)k_count * kHistBytes + (size_t)kWaves * 256 * sizeof(uint32_t) + (size_t)k_count * sizeof(EncodePar);
+size_t encode_lds_bytes(int k_count, int copies) {
+  return (size_t)k_count * copies * kHistBytes + (size_t)kWaves * 256 * sizeof(uint32_t) +
+         (size_t)k_count * sizeof(EncodePar);
+}
+
+// Copies of each learner's histogram, interleaved per bucket and picked by lane:
+// lanes that hit the same bucket in one instruction land on different words, so
+// concentrated code distributions (for example pseudo-gradients that are exactly
+// zero on untouched rows) do not serialize on one address.  Four copies up to 8
+// learners per launch (64 KB of histogram), two above.
+int encode_copies(int k_count) { return k_count <= 8 ? 4 : 2; }
+
+template <int R>
+hipError_t launch_encode_r(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
+  const size_t lds = encode_lds_bytes(a.k_count, R);
+  hipError_t e = allow_lds(k_encode<R>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_encode<R>, dim3(g.n_blocks), dim3(kBlock), lds, s, a, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
-  const size_t lds = encode_lds_bytes(a.k_count);
-  hipError_t e = allow_lds(k_encode, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_encode, dim3(g.n_blocks), dim3(kBlock), lds, s, a, g);
-  return hipGetLastError();
+  const int r = encode_copies(a.k_count);
+  if (r == 4) return launch_encode_r<4>(a, g, s);
+  if (r == 2) return launch_encode_r<2>(a, g, s);
+  return launch_encode_r<1>(a, g, s);
 }
 
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {

@@ -39,10 +39,23 @@ def case_inputs(name):
         kinds = ["vector", "const", "const", "vector", "const", "vector", "matrix", "matrix", "matrix"]
         cfg = workloads.custom("absent", sizes, 16, delta="laplace", delta_scale=7e-4, absent_p=0.25, kinds=kinds)
         return workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV, fragment=3)
+    if name == "sparse_k8":
+        # pseudo-gradients that are exactly zero on 90% of the elements (rows no
+        # learner touched): codes pile into one bucket
+        cfg = workloads.custom("sparse", [1 << 20, 4096 * 7 + 5], 8)
+        inp = workloads.fragment_inputs(cfg, [0, 1], DEV)
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(1234)
+        for i in range(8):
+            keep = torch.rand(inp.theta_L.shape[1], generator=gen, device=DEV) < 0.1
+            for (o, lo, n) in inp.tensors:
+                seg = inp.theta_L[i, lo:lo + n]
+                seg.copy_(torch.where(keep[lo:lo + n], seg, inp.theta_g[o:o + n]))
+        return inp
     raise KeyError(name)
 
 
-CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const"]
+CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const", "sparse_k8"]
 
 
 @pytest.mark.parametrize("name", CASES)
