@@ -30,7 +30,7 @@ int32_t ok() {
 
 // Target number of blocks per streaming launch: a few resident blocks per CU on
 // a 256-CU part, so that the tensor-aligned partition stays balanced.
-constexpr int64_t kTargetBlocks = 2048;
+constexpr int64_t kTargetBlocks = 4096;
 
 constexpr int64_t kMaxTensorNumel = (int64_t(1) << 32) - 1;
 constexpr int64_t kMaxOffset = (int64_t(1) << 38) - DLC_ALIGN_ELEMS;

@@ -27,6 +27,7 @@
 #include "dlc_internal.h"
 
 #include <cfloat>
+#include <type_traits>
 
 namespace dlc {
 namespace {
@@ -327,20 +328,21 @@ __global__ __launch_bounds__(64) void k_range(const QuantArgs a, const LaunchGeo
 // k_encode: codes + per-block LDS histogram for up to kLearnerChunk learners.
 //
 // Bucket index.  The definition is c = clip(floor(fl32(fl32(x - lo) / wd)), 0, 255).
-// With r = fl32(1 / wd) and q' = fl32(t * r), t = fl32(x - lo), both q' and the
-// correctly rounded quotient q = fl32(t / wd) lie within 1.5 * 2^-24 relative of
-// the exact t / wd, so |q' - q| <= 3 * 2^-24 * |t / wd|.  Wherever the result is not
-// clamped (|t / wd| < 257) that is below 2^-14, so floor(q') = floor(q) whenever the
-// fractional part of q' is at least 2^-14 away from 0 and from 1.  Only those rare
-// elements (about 1 in 8000) take the exact IEEE division.
+// With t = fl32(x - lo), r = fl32(1 / wd) and q' = fl32(t * r + 2^-14) (one fused
+// multiply-add), both q' - 2^-14 and the correctly rounded quotient q = fl32(t / wd)
+// lie within about 2^-24 |t / wd| of the exact t / wd, so |q' - 2^-14 - q| <=
+// 3 * 2^-24 * |t / wd|, below 2^-14 wherever the result is not clamped (|t / wd| <
+// 257).  Hence q lies in (q' - 2^-13, q'], and floor(q') = floor(q) whenever
+// fract(q') >= 2^-13.  Only the elements with fract(q') < 2^-13 (about 1 in 8000)
+// take the exact IEEE division; a wave redoes one element slot only when some lane
+// needs it there.
 //
-// Histogram: one 64-bit LDS atomic per element adds 2^44 (the count) plus the
-// element's position inside its bucket as a fixed-point integer (low 44 bits),
-// see hist_frac_bits.  Integer sums make the histogram exact and independent of
-// the order of the atomics.  Codes of a full tile are packed 4
-// per dword in the load layout, transposed through a per-wave LDS stage, and
-// written with 16-byte stores: one store instruction writes the wave's 1 KB of
-// codes contiguously.
+// Histogram: one 64-bit LDS atomic per element adds the count unit and the
+// element's position inside its bucket as a fixed-point integer, see
+// EncodePar.  Integer sums make the histogram exact and independent of the order
+// of the atomics.  Codes of a full tile are packed 4 per dword in the load layout,
+// transposed through a per-wave LDS stage, and written with 16-byte stores: one
+// store instruction writes the wave's 1 KB of codes contiguously.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float uniform_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
@@ -354,11 +356,12 @@ __device__ __forceinline__ double uniform_f64(double v) {
 }
 
 // Fraction bits s of the packed bucket-position sums for one (learner, tensor).
-// An element of bucket c contributes q = round((x_c - lo) * 2^s / wd - c * 2^s).
-// For buckets 0..254, q lies within [-2^12, 2^s + 2^12] (the fp32 bucket index
-// can misplace x by at most 3 * 2^-24 * 257 bucket widths); bucket 255 also holds
-// the values up to hi, i.e. q <= ((hi - lo) / wd - 255) * 2^s.  s is the largest
-// value <= kHistFracBits that keeps q + kHistBias below 2^27 (normally 26).
+// An element of bucket c contributes q = round((x_c - lo) * 2^s / wd) - c * 2^s
+// (plus a constant, see EncodePar).  For buckets 0..254, q lies within
+// [-2^12, 2^s + 2^12] (the fp32 bucket index can misplace x by at most
+// 3 * 2^-24 * 257 bucket widths); bucket 255 also holds the values up to hi, i.e.
+// q <= ((hi - lo) / wd - 255) * 2^s.  s is the largest value <= kHistFracBits that
+// keeps q + kHistBias below 2^27 (normally 26).
 __device__ __forceinline__ int hist_frac_bits(float lo, float hi, float wd) {
   const double ext = ((double)hi - (double)lo) / (double)wd - 255.0;
   const double top = ext > 1.0 ? ext : 1.0;
@@ -367,13 +370,30 @@ __device__ __forceinline__ int hist_frac_bits(float lo, float hi, float wd) {
   return s;
 }
 
+// Fixed-point bucket positions without integer conversions.  With scale = 2^s / wd,
+// B = -lo * scale and B_i = rint(B), the element's addend is the bit pattern of
+//   y = fl64(fl64(x_c * scale + (2^52 + 2^44 + B_i + kHistBias)) - c * 2^s)
+// The first fused multiply-add rounds to an integer (the spacing of doubles in
+// [2^52, 2^53) is 1), so y = 2^52 + 2^44 + v with v = rint(x_c * scale) + B_i -
+// c * 2^s + kHistBias in [0, 2^27); the second is exact.  Its bits are
+// kPosUnit * 2^44 + v: the low 44 bits carry v, the top 20 bits the odd constant
+// kPosUnit, so a sum of N addends holds N * kPosUnit mod 2^20 on top (N < 2^20
+// per block, recovered with the inverse kPosUnitInv) and the sum of v below.
+// The exact position (x_c - lo) * scale - c * 2^s is v - kHistBias + (B - B_i)
+// within 1/2: the codebook adds the constant B - B_i back.
+constexpr double kPosMagic = 0x1p52 + 0x1p44;
+constexpr uint64_t kPosUnit = 0x43301;  // top 20 bits of every addend
+constexpr uint64_t kPosUnitInv = 0x4cd01;  // kPosUnit * kPosUnitInv = 1 mod 2^20
+static_assert((kPosUnit * kPosUnitInv & 0xFFFFF) == 1, "count unit inverse");
+static_assert(kHistCountShift == 44, "addend layout");
+
 // Per-learner encode parameters, staged in LDS once per block.
 struct EncodePar {
   float lo, hi, wd, rcp;  // clip range, bucket width, fl32(1 / wd)
   double scale;           // 2^s / wd
-  double neg_lo_scale;    // -lo * 2^s / wd
-  double two_s;           // 2^s
-  double pad;
+  double magic;           // 2^52 + 2^44 + rint(-lo * scale) + kHistBias
+  double neg_two_s;       // -2^s
+  double origin_frac;     // -lo * scale - rint(-lo * scale)
 };
 
 __device__ __forceinline__ EncodePar make_encode_par(float4 r) {
@@ -382,112 +402,114 @@ __device__ __forceinline__ EncodePar make_encode_par(float4 r) {
   p.hi = r.y;
   p.wd = r.z;
   p.rcp = 0.0f;
-  p.scale = p.neg_lo_scale = p.two_s = p.pad = 0.0;
+  p.scale = p.magic = p.neg_two_s = p.origin_frac = 0.0;
   if (r.z >= FLT_MIN) {
     p.rcp = 1.0f / r.z;
     const int s = hist_frac_bits(r.x, r.y, r.z);
-    p.two_s = (double)(1ll << s);
-    p.scale = p.two_s / (double)r.z;
-    p.neg_lo_scale = -(double)r.x * p.scale;
+    const double two_s = (double)(1ll << s);
+    p.scale = two_s / (double)r.z;
+    const double b = -(double)r.x * p.scale;
+    const double bi = __builtin_rint(b);
+    p.magic = kPosMagic + (bi + (double)kHistBias);
+    p.neg_two_s = -two_s;
+    p.origin_frac = b - bi;
   }
   return p;
 }
 
+// Codes of one (learner, tile) item, packed 4 per dword in the load layout
+// (dword j of a lane holds the codes of float4 number f4_index(tid, j)), and the
+// item's histogram atomics.  FULL = every element of the tile is valid; otherwise
+// element e is valid iff its index is below n.
 template <bool FULL, int R>
-__device__ __forceinline__ void encode_tile(uint64_t* __restrict__ hist, uint32_t* __restrict__ st,
-                                            uint8_t* __restrict__ cp, const float (&gv)[kVec],
-                                            const float (&lv)[kVec], const EncodePar& par_lds, int tid,
-                                            int64_t n) {
+__device__ __forceinline__ void encode_codes(uint64_t* __restrict__ hist, const float (&gv)[kVec],
+                                             const float (&lv)[kVec], const EncodePar& par_lds, int tid,
+                                             int64_t n, uint32_t (&packed)[4]) {
+  static_assert((R & (R - 1)) == 0, "copies must be a power of two");
   // The parameters are the same for every lane: keep them in scalar registers.
   const float lo = uniform_f32(par_lds.lo), hi = uniform_f32(par_lds.hi), wd = uniform_f32(par_lds.wd);
   const float rcp = uniform_f32(par_lds.rcp);
-  const double scale = uniform_f64(par_lds.scale), neg_lo_scale = uniform_f64(par_lds.neg_lo_scale);
-  const double neg_two_s = -uniform_f64(par_lds.two_s);
-  uint32_t packed[4] = {0u, 0u, 0u, 0u};
-  if (wd >= FLT_MIN) {  // otherwise (zero variance) every code is 0 and no histogram is needed
-    constexpr float kNear = 0.5f - 0x1p-14f;
-    float x[kVec], fq[kVec];
-    bool near_any = false;
+  const double scale = uniform_f64(par_lds.scale), magic = uniform_f64(par_lds.magic);
+  const double neg_two_s = uniform_f64(par_lds.neg_two_s);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) packed[j] = 0u;
+  if (!(wd >= FLT_MIN)) return;  // zero variance: every code is 0 and no histogram is needed
+  constexpr float kShift = 0x1p-14f, kNearWin = 0x1p-13f;
+  float x[kVec], qs[kVec];
+  bool near_any = false;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    x[e] = gv[e] - lv[e];
+    qs[e] = __builtin_fmaf(x[e] - lo, rcp, kShift);
+    near_any |= __builtin_amdgcn_fractf(qs[e]) < kNearWin;
+  }
+  // Rare: some lane holds an element within 2^-14 of a bucket edge.
+  if (__builtin_expect(__builtin_amdgcn_ballot_w64(near_any) != 0, 0)) {
 #pragma unroll
     for (int e = 0; e < kVec; ++e) {
-      x[e] = gv[e] - lv[e];
-      const float q = (x[e] - lo) * rcp;
-      fq[e] = floorf(q);
-      near_any |= fabsf((q - fq[e]) - 0.5f) > kNear;
-    }
-    // Rare: some element of the wave lies within 2^-14 of a bucket edge; redo those
-    // with the correctly rounded division (one wave-uniform branch per tile).
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(near_any) != 0, 0)) {
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) {
-        const float t = x[e] - lo;
-        const float q = t * rcp;
-        const bool near = fabsf((q - fq[e]) - 0.5f) > kNear;
-        const float exact = floorf(t / wd);
-        fq[e] = near ? exact : fq[e];
+      const bool near = __builtin_amdgcn_fractf(qs[e]) < kNearWin;
+      if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        const float exact = floorf((x[e] - lo) / wd);
+        qs[e] = near ? exact : qs[e];
       }
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int e = 4 * j + c;
-        const float cf = __builtin_amdgcn_fmed3f(fq[e], 0.0f, 255.0f);
-        const uint32_t code = (uint32_t)cf;
-        if (FULL || tail_valid(tid, j, c, n)) {
-          // position of the clipped value inside its bucket, fixed point
-          const double xc = (double)__builtin_amdgcn_fmed3f(x[e], lo, hi);
-          const double off = __fma_rn((double)cf, neg_two_s, neg_lo_scale);
-          const int32_t q = (int32_t)__builtin_rint(__fma_rn(xc, scale, off));
-          const uint64_t add = ((uint64_t)1 << kHistCountShift) + (uint32_t)(q + kHistBias);
-          atomicAdd(reinterpret_cast<unsigned long long*>(hist + (code * R + (tid & (R - 1)))), (unsigned long long)add);
-        }
-        w |= code << (8 * c);
-      }
-      packed[j] = w;
     }
   }
-  if (FULL) {
-    const int lane = tid & 63, wave = tid >> 6;
+  // this lane's copy of the histogram, as a byte address
+  char* const hl = reinterpret_cast<char*>(hist) + 8 * (tid & (R - 1));
+  constexpr int kShiftR = 3 + (R == 1 ? 0 : R == 2 ? 1 : R == 4 ? 2 : 3);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) st[j * 64 + lane] = packed[j];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const vu4 v = *reinterpret_cast<const vu4*>(st + 4 * lane);
-    *reinterpret_cast<vu4*>(cp + 1024 * wave + 16 * lane) = v;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  } else {
+  for (int j = 0; j < 4; ++j) {
+    uint32_t w = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (tail_valid(tid, j, c, n)) cp[elem_index(tid, j, c)] = (uint8_t)(packed[j] >> (8 * c));
+    for (int c = 0; c < 4; ++c) {
+      const int e = 4 * j + c;
+      const uint32_t code = (uint32_t)__builtin_amdgcn_fmed3f(qs[e], 0.0f, 255.0f);
+      if (FULL || tail_valid(tid, j, c, n)) {
+        const double xc = (double)__builtin_amdgcn_fmed3f(x[e], lo, hi);
+        const double y = __fma_rn((double)code, neg_two_s, __fma_rn(xc, scale, magic));
+        atomicAdd(reinterpret_cast<unsigned long long*>(hl + (code << kShiftR)),
+                  __builtin_bit_cast(unsigned long long, y));
       }
+      w |= code << (8 * c);
     }
+    packed[j] = w;
   }
 }
 
-// Items stream through a ring of kEncRing register buffers.  The items of a
-// block are its full tiles in order, each tile being theta_g followed by the
-// k_count learners; item p + kEncRing - 1 is requested while item p is
-// processed, across tile boundaries, so no item is ever padded or read twice
-// (except up to kEncRing - 1 repeated requests at the very end of the block).
-// Per-learner {lo, hi, wd, 1/wd, fixed-point scale} are staged in LDS once per
-// block.
-constexpr int kEncRing = 3;
+// Codes of a full tile through a buffer descriptor covering the tile's 4096 bytes
+// (zero records when !valid: the stores are dropped).  Dword j of every lane of a
+// wave covers 256 consecutive bytes, so each non-temporal store writes whole
+// cache lines.
+__device__ __forceinline__ void store_codes(uint8_t* cp, bool valid, int tid, const uint32_t (&packed)[4]) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(cp, (short)0, valid ? kTile : 0, kBufferWord3);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_buffer_store_b32(packed[j], r, f4_index(tid, j) * 4, 0, 2);
+}
+
+// Order of work.  A block's full tiles form groups of kGroup consecutive tiles.
+// For each group, theta_g's kGroup tiles are held in registers while every
+// learner is encoded against them, one learner at a time; a learner's codes of the
+// whole group (kGroup * 4 KB, contiguous) leave in one burst of stores once its
+// last tile is done.  Long runs of consecutive bytes per block and learner keep
+// the HBM write stream efficient next to the much larger read stream.
+// Learner tiles stream through a ring of kGroup register buffers: the tile three
+// items ahead is requested before a tile is encoded, across learner and group
+// boundaries.  theta_g's tile u of the next group is requested into its own
+// registers as soon as the group's last learner has encoded tile u.  A request for
+// a tile beyond the block's full tiles (a partial last group, or past the end) is a
+// null request: no memory traffic, and the tile is skipped.  Every load and store
+// is unconditional, so the compiler's wait counts stay exact.
+// Per-learner {lo, hi, wd, 1/wd, fixed-point constants} are staged in LDS once
+// per block.
+constexpr int kGroup = 4;
 
 template <int R>
 __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const LaunchGeom g) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int kc = a.k_count;
   uint64_t* hist = reinterpret_cast<uint64_t*>(smem);
-  uint32_t* stage = reinterpret_cast<uint32_t*>(smem + kc * R * kHistBytes);
-  EncodePar* par = reinterpret_cast<EncodePar*>(stage + kWaves * 256);
-  const int tid = threadIdx.x, wave = tid >> 6;
+  EncodePar* par = reinterpret_cast<EncodePar*>(smem + kc * R * kHistBytes);
+  const int tid = threadIdx.x;
 
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
@@ -496,62 +518,84 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
   if (tid < kc) par[tid] = make_encode_par(a.range[(size_t)a.learner[a.k_base + tid] * g.n_tensors_call + rrow]);
   __syncthreads();
 
-  const float* __restrict__ tg = a.theta_g + td.offset();
-  uint32_t* st = stage + wave * 256;
+  const float* __restrict__ tg = a.theta_g + td.offset() + sp.begin;
   auto codes_of = [&](int k) {
-    return a.codes + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset();
+    return a.codes + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset() + sp.begin;
   };
 
   const int64_t n_full = (sp.end - sp.begin) / kTile;
   if (n_full > 0) {
-    const int items_per_tile = kc + 1;
-    const int64_t total = n_full * items_per_tile;
-    const int64_t last = sp.begin + (n_full - 1) * kTile;
-    // request cursor (tile base, item) runs kEncRing - 1 items ahead of the work cursor
-    int64_t rb = sp.begin;
-    int ri = 0;
-    auto request = [&](float (&dst)[kVec]) {
-      const float* src = ri == 0 ? tg + rb : learner_row(a, ri - 1, td) + rb;
-      load_full(src, tid, dst);
-      if (++ri == items_per_tile) {
-        ri = 0;
-        rb = rb < last ? rb + kTile : last;  // past the end: repeat the last tile
-      }
+    const int64_t n_groups = (n_full + kGroup - 1) / kGroup;
+    // tile u of group grp of stream s (0 = theta_g, s >= 1 = learner s - 1)
+    auto request = [&](float (&dst)[kVec], int64_t grp, int s, int u) {
+      const int64_t tile = grp * kGroup + u;
+      const bool valid = tile < n_full;
+      const float* base = s == 0 ? tg : learner_row(a, s - 1, td) + sp.begin;
+      load_tile_rsrc(tile_rsrc(base + (valid ? tile : 0) * kTile, valid), tid, dst);
     };
-    float gv[kVec], ring[kEncRing][kVec];
+    float gv[kGroup][kVec], ring[kGroup][kVec];
+    // Prologue in the order a pass leaves its requests behind: theta_g's tiles,
+    // the first three learner tiles, then one pass worth of (null) code stores.
+    // Every way into the learner loop then carries the same sequence of memory
+    // operations, so the static wait counts at each tile's first use fit all of
+    // them without draining the ring.
 #pragma unroll
-    for (int i = 0; i < kEncRing - 1; ++i) request(ring[i]);
-    int64_t wb = sp.begin;
-    int wi = 0;
-    for (int64_t p0 = 0; p0 < total; p0 += kEncRing) {
+    for (int u = 0; u < kGroup; ++u) request(gv[u], 0, 0, u);
 #pragma unroll
-      for (int u = 0; u < kEncRing; ++u) {
-        if (p0 + u < total) {
-          request(ring[(u + kEncRing - 1) % kEncRing]);
-          if (wi == 0) {
+    for (int u = 0; u < kGroup - 1; ++u) request(ring[u], 0, 1, u);
+    {
+      const uint32_t zero[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int e = 0; e < kVec; ++e) gv[e] = ring[u][e];
+      for (int u = 0; u < kGroup; ++u) store_codes(codes_of(0), false, tid, zero);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t grp = 0; grp < n_groups; ++grp) {
+      const int64_t left = n_full - grp * kGroup;
+      const int valid = left < kGroup ? (int)left : kGroup;
+      // learner k over the group; kLast: the group's last learner, whose look-ahead
+      // runs into the next group
+      auto pass = [&](int k, auto last_tag) {
+        constexpr bool kLast = decltype(last_tag)::value;
+        uint32_t cw[kGroup][4];
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) {
+          if (u == 0) request(ring[kGroup - 1], grp, k + 1, kGroup - 1);
+          else if (kLast) request(ring[u - 1], grp + 1, 1, u - 1);
+          else request(ring[u - 1], grp, k + 2, u - 1);
+          if (u < valid) {
+            encode_codes<true, R>(hist + k * R * kBuckets, gv[u], ring[u], par[k], tid, kTile, cw[u]);
           } else {
-            const int k = wi - 1;
-            encode_tile<true, R>(hist + k * R * kBuckets, st, codes_of(k) + wb, gv, ring[u], par[k], tid, kTile);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) cw[u][j] = 0u;
           }
-          if (++wi == items_per_tile) {
-            wi = 0;
-            wb += kTile;
-          }
+          if (kLast) request(gv[u], grp + 1, 0, u);
         }
-      }
+        uint8_t* cp = codes_of(k) + grp * kGroup * kTile;
+#pragma unroll
+        for (int u = 0; u < kGroup; ++u) store_codes(cp + u * kTile, u < valid, tid, cw[u]);
+      };
+      for (int k = 0; k < kc - 1; ++k) pass(k, std::false_type{});
+      pass(kc - 1, std::true_type{});
     }
   }
-  const int64_t full_end = sp.begin + n_full * kTile;
-  if (full_end < sp.end) {
-    const int64_t n = sp.end - full_end;
+  const int64_t full_len = n_full * kTile;
+  if (sp.begin + full_len < sp.end) {
+    const int64_t n = sp.end - sp.begin - full_len;
     float gv[kVec];
-    load_tail(tg + full_end, tid, n, gv);
+    load_tail(tg + full_len, tid, n, gv);
     for (int k = 0; k < kc; ++k) {
       float lv[kVec];
-      load_tail(learner_row(a, k, td) + full_end, tid, n, lv);
-      encode_tile<false, R>(hist + k * R * kBuckets, st, codes_of(k) + full_end, gv, lv, par[k], tid, n);
+      load_tail(learner_row(a, k, td) + sp.begin + full_len, tid, n, lv);
+      uint32_t cw[4];
+      encode_codes<false, R>(hist + k * R * kBuckets, gv, lv, par[k], tid, n, cw);
+      uint8_t* cp = codes_of(k) + full_len;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (tail_valid(tid, j, c, n)) cp[elem_index(tid, j, c)] = (uint8_t)(cw[j] >> (8 * c));
+        }
+      }
     }
   }
 
@@ -562,7 +606,9 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
     uint64_t v = 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) v += hist[i * R + r];
-    dst[i] = v;
+    // count = (N * kPosUnit mod 2^20) * kPosUnitInv mod 2^20; positions stay below
+    const uint64_t count = ((v >> kHistCountShift) * kPosUnitInv) & ((1ull << (64 - kHistCountShift)) - 1);
+    dst[i] = (count << kHistCountShift) | (v & ((1ull << kHistCountShift) - 1));
   }
 }
 
@@ -621,8 +667,8 @@ __global__ __launch_bounds__(kBuckets * kCodebookGroups) void k_codebook(const Q
   if (!(r.z >= FLT_MIN)) {
     out = r.w;
   } else if (N > 0) {
-    const int s = hist_frac_bits(r.x, r.y, r.z);
-    const double frac = (double)Q / ((double)N * (double)(1ll << s));
+    const EncodePar par = make_encode_par(r);
+    const double frac = ((double)Q / (double)N + par.origin_frac) / -par.neg_two_s;
     out = (float)((double)r.x + (double)r.z * ((double)c + frac));
   } else {
     out = (float)((double)r.x + ((double)c + 0.5) * (double)r.z);
@@ -796,8 +842,7 @@ hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) 
 }
 
 size_t encode_lds_bytes(int k_count, int copies) {
-  return (size_t)k_count * copies * kHistBytes + (size_t)kWaves * 256 * sizeof(uint32_t) +
-         (size_t)k_count * sizeof(EncodePar);
+  return (size_t)k_count * copies * kHistBytes + (size_t)k_count * sizeof(EncodePar);
 }
 
 // Copies of each learner's histogram, interleaved per bucket and picked by lane:
