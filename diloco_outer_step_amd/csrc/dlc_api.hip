@@ -44,14 +44,16 @@ struct Partition {
 
 // Split the call's tensors into launches of at most kMaxTensorsPerLaunch tensors;
 // each tensor gets ceil(tiles / tiles_per_block) blocks, tiles_per_block chosen
-// from the whole call so that the call has about kTargetBlocks blocks, and at
-// most max_tiles.
-Partition make_partition(const dlc_tensor* t, int32_t n, int64_t max_tiles) {
+// from the whole call so that the call has about target_blocks blocks, at most
+// max_tiles, and rounded up to a multiple of tile_multiple.
+Partition make_partition(const dlc_tensor* t, int32_t n, int64_t max_tiles, int64_t target_blocks = kTargetBlocks,
+                         int64_t tile_multiple = 1) {
   Partition p;
   int64_t total_tiles = 0;
   for (int32_t i = 0; i < n; ++i) total_tiles += (t[i].numel + dlc::kTile - 1) / dlc::kTile;
-  int64_t tpb = std::max<int64_t>(1, (total_tiles + kTargetBlocks - 1) / kTargetBlocks);
+  int64_t tpb = std::max<int64_t>(1, (total_tiles + target_blocks - 1) / target_blocks);
   tpb = std::min(tpb, max_tiles);
+  tpb = (tpb + tile_multiple - 1) / tile_multiple * tile_multiple;
   for (int32_t s = 0; s < n; s += dlc::kMaxTensorsPerLaunch) {
     dlc::LaunchGeom g;
     std::memset(&g, 0, sizeof(g));
@@ -343,7 +345,9 @@ int32_t dlc_merge_outer_step(float* theta_global, float* momentum, const uint8_t
   a.n_present = kp;
   a.lr = lr;
   a.beta = beta;
-  const Partition p = make_partition(tensors, n_tensors, kUnlimitedTiles);
+  // merge blocks work on kMergeTiles tiles side by side
+  const Partition p = make_partition(tensors, n_tensors, kUnlimitedTiles, kTargetBlocks / dlc::kMergeTiles,
+                                     dlc::kMergeTiles);
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   for (const dlc::LaunchGeom& g : p.launches) {
     hipError_t e = dlc::launch_merge(a, g, s);

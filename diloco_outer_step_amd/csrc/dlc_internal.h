@@ -32,6 +32,9 @@ constexpr int kMaxEncodeTiles = 32;
 constexpr int kHistFracBits = 26;
 constexpr int kHistBias = 1 << 13;
 constexpr int kHistCountShift = 44;
+// Tiles a merge block works on side by side (kBlock threads each).  The kernel
+// supports 1, 2 and 4; wider blocks measured slower on the 1B parameter set.
+constexpr int kMergeTiles = 1;
 constexpr int kStatsChunk = 14;           // learners per statistics launch (register accumulators)
 
 // 16 bytes per tensor so that up to kMaxTensorsPerLaunch descriptors fit in the

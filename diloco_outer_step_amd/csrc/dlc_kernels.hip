@@ -73,19 +73,6 @@ __device__ __forceinline__ int tensor_block_end(const LaunchGeom& g, int t) {
 // block.
 __device__ __forceinline__ int f4_index(int tid, int j) { return (tid & ~63) * 4 + j * 64 + (tid & 63); }
 
-// 16 floats of a full tile, 4 coalesced non-temporal float4 loads.
-__device__ __forceinline__ void load_full(const float* __restrict__ p, int tid, float (&v)[kVec]) {
-  const vf4* q = reinterpret_cast<const vf4*>(p);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const vf4 x = __builtin_nontemporal_load(q + f4_index(tid, j));
-    v[4 * j + 0] = x.x;
-    v[4 * j + 1] = x.y;
-    v[4 * j + 2] = x.z;
-    v[4 * j + 3] = x.w;
-  }
-}
-
 // 16 floats of a full tile through a buffer descriptor covering just that tile
 // (non-temporal).  A descriptor with zero records makes every load return zeros
 // without touching memory: a "null" request that still counts as a memory
@@ -120,19 +107,6 @@ __device__ __forceinline__ void load_tail(const float* __restrict__ p, int tid, 
     for (int c = 0; c < 4; ++c) {
       v[4 * j + c] = tail_valid(tid, j, c, n) ? p[elem_index(tid, j, c)] : 0.0f;
     }
-  }
-}
-
-__device__ __forceinline__ void store_full(float* __restrict__ p, int tid, const float (&v)[kVec]) {
-  vf4* q = reinterpret_cast<vf4*>(p);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    vf4 x;
-    x.x = v[4 * j + 0];
-    x.y = v[4 * j + 1];
-    x.z = v[4 * j + 2];
-    x.w = v[4 * j + 3];
-    __builtin_nontemporal_store(x, q + f4_index(tid, j));
   }
 }
 
@@ -705,24 +679,54 @@ __device__ __forceinline__ void load_codes_rsrc(const uint8_t* cp, bool valid, i
   for (int j = 0; j < 4; ++j) cw[j] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, f4_index(tid, j) * 4, 0, 2);
 }
 
-// Code words of (learner, tile) items stream through a ring of kMergeRing
-// registers (item i + kMergeRing - 1 is requested while item i is looked up),
-// items per tile padded to a multiple of the ring with null requests, every
-// request unconditional.
-// theta and momentum of a tile are requested when the tile starts; they are
-// needed only after every learner has been looked up.
-constexpr int kMergeRing = 4;
+// theta or momentum of one tile through a buffer descriptor covering the tile's
+// 16 KB (zero records when !valid: loads return zeros, stores are dropped).
+__device__ __forceinline__ void store_tile_rsrc(__amdgpu_buffer_rsrc_t r, int tid, const float (&v)[kVec]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    vf4 x;
+    x.x = v[4 * j + 0];
+    x.y = v[4 * j + 1];
+    x.z = v[4 * j + 2];
+    x.w = v[4 * j + 3];
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(vu4, x), r, f4_index(tid, j) * 16, 0, 2);
+  }
+}
 
-__global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const LaunchGeom g) {
+// A merge block is kMergeTiles groups of kBlock threads; group q works on tile
+// kMergeTiles * s + q of the block's span in round s, so every learner's codes,
+// theta and momentum move in runs of kMergeTiles * 4 KB (codes) and
+// kMergeTiles * 16 KB per block.  Tiles past the block's full tiles are null
+// requests and dropped stores (wave-uniform: a group is 4 whole waves).
+// Code words of (learner, round) items stream through a ring of kMergeRing
+// registers (item i + kMergeRing - 1 is requested while item i is looked up),
+// items per round padded to a multiple of the ring with null requests, every
+// request unconditional.
+// theta and momentum of a round are requested when the round starts; they are
+// needed only after every learner has been looked up.
+// NR > 0: every round has exactly NR ring rounds of kMergeRing items (up to
+// 4 * NR learners), so the learner loop unrolls and every round issues the same
+// sequence of memory operations; the prologue ends with a round's worth of (null)
+// stores, so the static wait counts fit the first round as well as the others.
+// NR = 0: any number of learners, ring rounds counted at run time.
+constexpr int kMergeRing = 4;
+constexpr int kMergeMaxRounds = 4;
+constexpr int kMergeBlock = kBlock * kMergeTiles;
+
+template <int NR>
+__global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_merge(
+    const MergeArgs a, const LaunchGeom g) {
   extern __shared__ __align__(16) unsigned char smem[];
   double* tab = reinterpret_cast<double*>(smem);
-  const int tid = threadIdx.x;
+  // tile slot of this thread's group (whole waves: keep it in a scalar register)
+  const int q = __builtin_amdgcn_readfirstlane(threadIdx.x / kBlock);
+  const int tid = threadIdx.x % kBlock;  // thread within the group
   const int kp = a.n_present;
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
   const size_t trow = (size_t)g.t_base + sp.t;
 
-  for (int i = tid; i < kp * kBuckets; i += kBlock) {
+  for (int i = threadIdx.x; i < kp * kBuckets; i += kMergeBlock) {
     const int k = i >> 8, c = i & (kBuckets - 1);
     const float cb = a.codebook[((size_t)a.learner[k] * g.n_tensors_call + trow) * kBuckets + c];
     tab[i] = a.w_hat[k] * (double)cb;
@@ -736,30 +740,45 @@ __global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const Launc
 
   const int64_t n_full = (sp.end - sp.begin) / kTile;
   if (n_full > 0) {
-    const int items = (kp + kMergeRing - 1) / kMergeRing * kMergeRing;
-    const int64_t last = sp.begin + (n_full - 1) * kTile;
+    const int items = NR > 0 ? NR * kMergeRing : (kp + kMergeRing - 1) / kMergeRing * kMergeRing;
+    const int64_t n_rounds = (n_full + kMergeTiles - 1) / kMergeTiles;
+    // this group's tile of round r (element offset in the tensor) and whether it is full
+    auto tile_of = [&](int64_t r) { return r * kMergeTiles + q; };
+    auto request = [&](uint32_t (&dst)[4], int64_t r, int i) {
+      const int64_t tile = tile_of(r);
+      const bool valid = i < kp && tile < n_full;
+      load_codes_rsrc(codes_of(i < kp ? i : kp - 1) + sp.begin + (valid ? tile : 0) * kTile, valid, tid, dst);
+    };
     uint32_t ring[kMergeRing][4];
 #pragma unroll
-    for (int i = 0; i < kMergeRing - 1; ++i) load_codes_rsrc(codes_of(i < kp ? i : kp - 1) + sp.begin, i < kp, tid, ring[i]);
-    for (int64_t base = sp.begin; base <= last; base += kTile) {
-      const int64_t nbase = base < last ? base + kTile : last;
+    for (int i = 0; i < kMergeRing - 1; ++i) request(ring[i], 0, i);
+    if (NR > 0) {
+      const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(th, (short)0, 0, kBufferWord3);
+      const float zero[kVec] = {};
+      store_tile_rsrc(none, tid, zero);
+      store_tile_rsrc(none, tid, zero);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t r = 0; r < n_rounds; ++r) {
+      const int64_t tile = tile_of(r);
+      const bool valid = tile < n_full;
+      const int64_t base = sp.begin + (valid ? tile : 0) * kTile;
+      const __amdgpu_buffer_rsrc_t rt = tile_rsrc(th + base, valid), rv = tile_rsrc(mv + base, valid);
       float tv[kVec], vv[kVec];
-      load_full(th + base, tid, tv);
-      load_full(mv + base, tid, vv);
+      load_tile_rsrc(rt, tid, tv);
+      load_tile_rsrc(rv, tid, vv);
       double acc[kVec];
 #pragma unroll
       for (int e = 0; e < kVec; ++e) acc[e] = 0.0;
+      constexpr int kRoundsUnroll = NR > 0 ? NR : 1;
+#pragma unroll kRoundsUnroll
       for (int i0 = 0; i0 < items; i0 += kMergeRing) {
 #pragma unroll
         for (int u = 0; u < kMergeRing; ++u) {
           const int i = i0 + u;
-          int ip = i + kMergeRing - 1;
-          int64_t pb = base;
-          if (ip >= items) {
-            ip -= items;
-            pb = nbase;
-          }
-          load_codes_rsrc(codes_of(ip < kp ? ip : kp - 1) + pb, ip < kp, tid, ring[(u + kMergeRing - 1) % kMergeRing]);
+          const int ip = i + kMergeRing - 1;
+          if (ip < items) request(ring[(u + kMergeRing - 1) % kMergeRing], r, ip);
+          else request(ring[(u + kMergeRing - 1) % kMergeRing], r + 1, ip - items);
           if (i < kp) {
             const double* tk = tab + i * kBuckets;
 #pragma unroll
@@ -771,12 +790,12 @@ __global__ __launch_bounds__(kBlock) void k_merge(const MergeArgs a, const Launc
         }
       }
       nesterov16(tv, vv, acc, lr, beta);
-      store_full(th + base, tid, tv);
-      store_full(mv + base, tid, vv);
+      store_tile_rsrc(rt, tid, tv);
+      store_tile_rsrc(rv, tid, vv);
     }
   }
   const int64_t full_end = sp.begin + n_full * kTile;
-  if (full_end < sp.end) {
+  if (q == 0 && full_end < sp.end) {
     const int64_t n = sp.end - full_end;
     float tv[kVec], vv[kVec];
     load_tail(th + full_end, tid, n, tv);
@@ -873,12 +892,24 @@ hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) {
+template <int NR>
+hipError_t launch_merge_r(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) {
   const size_t lds = (size_t)a.n_present * kBuckets * sizeof(double);
-  hipError_t e = allow_lds(k_merge, lds);
+  hipError_t e = allow_lds(k_merge<NR>, lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_merge, dim3(g.n_blocks), dim3(kBlock), lds, s, a, g);
+  hipLaunchKernelGGL(k_merge<NR>, dim3(g.n_blocks), dim3(kMergeBlock), lds, s, a, g);
   return hipGetLastError();
+}
+
+hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) {
+  static_assert(kMergeMaxRounds == 4, "one instantiation per round count");
+  switch ((a.n_present + kMergeRing - 1) / kMergeRing) {
+    case 1: return launch_merge_r<1>(a, g, s);
+    case 2: return launch_merge_r<2>(a, g, s);
+    case 3: return launch_merge_r<3>(a, g, s);
+    case 4: return launch_merge_r<4>(a, g, s);
+    default: return launch_merge_r<0>(a, g, s);
+  }
 }
 
 }  // namespace dlc
