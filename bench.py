@@ -26,13 +26,17 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
-KERNEL_SOURCE = os.path.join(ROOT, "diloco_outer_step_amd", "csrc", "dlc_kernels.hip")
+# the kernels and the block partition that launches them: both shape the HBM traffic
+KERNEL_SOURCES = [os.path.join(ROOT, "diloco_outer_step_amd", "csrc", f) for f in ("dlc_kernels.hip", "dlc_api.hip")]
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel, workload):
