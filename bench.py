@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--workload", default="c3", choices=["c1", "c2", "c3", "c4", "c5k1", "c5k16"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 10B-fragment line")
+    ap.add_argument("--reported", action="store_true",
+                    help="time the reported, ungated sets (4096^2 cold, 24-fragment cycles of the 135M set "
+                         "and of the edge mix) and print them as one JSON line")
+    ap.add_argument("--reported-only", default=None, help="comma-separated subset of c1,c2,c5k1,c5k16")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a device-to-device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -153,6 +157,132 @@ def time_workload(key, steps, warmup, device):
     return out
 
 
+class FragmentCall:
+    """The three calls of one fragment's outer step on shared theta, momentum and
+    codes buffers (per-fragment range, codebook and workspace)."""
+
+    def __init__(self, inp, sel, theta, mom, codes, lr, beta):
+        import diloco_outer_step_amd as dlc
+        self.dlc = dlc
+        self.inp, self.theta, self.mom, self.codes = inp, theta, mom, codes
+        self.tensors = [inp.tensors[t] for t in sel]
+        k = inp.theta_L.shape[0]
+        _, self.cb, self.rng = dlc.outputs_for(k, 64, len(self.tensors), inp.theta_L.device)
+        self.ws = dlc.alloc_workspace(k, self.tensors, inp.theta_L.device)
+        self.lr, self.beta = lr, beta
+        self.n_params = sum(n for _, _, n in self.tensors)
+        self.k_present = sum(1 for p in inp.present if p)
+
+    def __call__(self):
+        d, inp = self.dlc, self.inp
+        d.dlc_quantize_range(self.theta, inp.theta_L, self.tensors, self.rng, self.ws, present=inp.present)
+        d.dlc_quantize_encode(self.theta, inp.theta_L, self.tensors, self.rng, self.codes, self.cb, self.ws,
+                              present=inp.present)
+        d.dlc_merge_outer_step(self.theta, self.mom, self.codes, self.cb, inp.weights, self.tensors, self.lr,
+                               self.beta)
+
+
+def time_calls(calls, reps, warmup, before=None):
+    """Median ms of each call over reps rounds (events on the launch stream); the
+    optional `before` runs untimed ahead of every call."""
+    import statistics
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        for c in calls:
+            c()
+    torch.cuda.synchronize()
+    ms = [[] for _ in calls]
+    for _ in range(reps):
+        for j, c in enumerate(calls):
+            if before is not None:
+                before()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            c()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms[j].append(e0.elapsed_time(e1))
+    return [statistics.median(m) for m in ms]
+
+
+def fragment_cycle(key, device, reps=5, warmup=2):
+    """Every fragment of the P-fragment plan merged in turn (one call each)."""
+    import torch
+    import diloco_outer_step_amd as dlc
+    import workloads
+    cfg = workloads.config(key)
+    ids = list(range(len(cfg.tensors)))
+    frag, _ = dlc.dlc_fragment_plan([s.numel for s in cfg.tensors], cfg.n_fragments)
+    per, total_params, total_bytes = [], 0, 0
+    if cfg.absent_p == 0.0:
+        inp = workloads.fragment_inputs(cfg, ids, device)
+        theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+        codes = torch.empty(inp.theta_L.shape, dtype=torch.uint8, device=device)
+        calls = [FragmentCall(inp, [t for t in ids if frag[t] == p], theta, mom, codes, cfg.lr, cfg.beta)
+                 for p in range(cfg.n_fragments) if any(f == p for f in frag)]
+        ms = time_calls(calls, reps, warmup)
+        for c, m in zip(calls, ms):
+            per.append(m)
+            total_params += c.n_params
+            total_bytes += (24 + 10 * c.k_present) * c.n_params
+        del calls, inp, theta, mom, codes
+    else:
+        # learners absent per fragment: each fragment has its own replicas
+        for p in range(cfg.n_fragments):
+            sel = [t for t in ids if frag[t] == p]
+            if not sel:
+                continue
+            inp = workloads.fragment_inputs(cfg, sel, device, fragment=p)
+            theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+            codes = torch.empty(inp.theta_L.shape, dtype=torch.uint8, device=device)
+            c = FragmentCall(inp, list(range(len(sel))), theta, mom, codes, cfg.lr, cfg.beta)
+            per.append(time_calls([c], reps, warmup)[0])
+            total_params += c.n_params
+            total_bytes += (24 + 10 * c.k_present) * c.n_params
+            del c, inp, theta, mom, codes
+            torch.cuda.empty_cache()
+    cycle_ms = sum(per)
+    return dict(workload=cfg.title, fragments=len(per), cycle_ms=cycle_ms, fragment_ms=per,
+                params=total_params, params_per_s=total_params / (cycle_ms * 1e-3),
+                hbm_gbps=total_bytes / (cycle_ms * 1e-3) / 1e9,
+                hbm_frac=total_bytes / (cycle_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS)
+
+
+def single_call_cold(key, device, reps=20, warmup=3, scratch_bytes=512 << 20):
+    """One call over the whole set, median of reps, each after a scratch write
+    large enough to evict the caches (256 MB Infinity Cache)."""
+    import torch
+    import workloads
+    cfg = workloads.config(key)
+    ids = list(range(len(cfg.tensors)))
+    inp = workloads.fragment_inputs(cfg, ids, device)
+    theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+    codes = torch.empty(inp.theta_L.shape, dtype=torch.uint8, device=device)
+    c = FragmentCall(inp, ids, theta, mom, codes, cfg.lr, cfg.beta)
+    scratch = torch.empty(scratch_bytes // 4, dtype=torch.float32, device=device)
+    ms = time_calls([c], reps, warmup, before=lambda: scratch.fill_(1.0))[0]
+    b = (24 + 10 * c.k_present) * c.n_params
+    return dict(workload=cfg.title, ms=ms, params=c.n_params, params_per_s=c.n_params / (ms * 1e-3),
+                hbm_gbps=b / (ms * 1e-3) / 1e9, hbm_frac=b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                cold_cache=f"{scratch_bytes >> 20} MB scratch write before each call")
+
+
+def reported(device, only=None):
+    """The parameter sets that are reported but not gated: the 4096^2 tensor (cold
+    cache), and full 24-fragment cycles of the 135M set and of the edge mix."""
+    keys = only.split(",") if only else ["c1", "c2", "c5k1", "c5k16"]
+    out = {}
+    if "c1" in keys:
+        out["c1"] = single_call_cold("c1", device)
+        print(f"# c1 {out['c1']['ms']:.3f} ms", file=sys.stderr, flush=True)
+    for key in [k for k in keys if k != "c1"]:
+        out[key] = fragment_cycle(key, device)
+        print(f"# {key} cycle {out[key]['cycle_ms']:.3f} ms over {out[key]['fragments']} fragments",
+              file=sys.stderr, flush=True)
+    return out
+
+
 def copy_probe(device, nbytes=1 << 32, reps=5):
     import torch
     a = torch.empty(nbytes // 4, dtype=torch.float32, device=device)
@@ -200,10 +330,114 @@ def cpu_baseline(res, budget_params=100_000_000):
     t0 = time.perf_counter()
     oracle.outer_step(th, mo, tl, stride, sel, inp.weights, inp.present, res["cfg"].lr, res["cfg"].beta)
     dt = time.perf_counter() - t0
-    return dict(value=total / dt, unit="params/s", cores=1, kind="oracle",
-                sample=f"{len(sel)} of the workload's tensors ({total} params, K={res['k_present']}) "
-                       f"through oracle.outer_step (numpy, fp64, one thread); {dt:.1f} s",
-                seconds=dt, numpy=np.__version__, cpu=cpu_model())
+    out = dict(value=total / dt, unit="params/s", cores=1, kind="oracle",
+               gbps=total * res["bytes_per_param"] / dt / 1e9,
+               sample=f"{len(sel)} of the workload's tensors ({total} params, K={res['k_present']}) "
+                      f"through oracle.outer_step (numpy, fp64, one thread); {dt:.1f} s",
+               seconds=dt, numpy=np.__version__, cpu=cpu_model())
+    try:
+        out["parallel"] = cpu_baseline_parallel(res)
+    except Exception as e:  # the single-process figure stands on its own
+        out["parallel"] = {"error": f"{type(e).__name__}: {e}"}
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The oracle on a pool of host processes: (tensor, learner) quantization units,
+# then one merge + Nesterov unit per tensor.  Workers are spawned (they never
+# touch the GPU) and share the inputs through memory-mapped files.
+_POOL = {}
+
+
+def _pool_attach(spec):
+    import numpy as np
+    for name, (path, shape, dtype) in spec.items():
+        _POOL[name] = np.memmap(path, dtype=dtype, mode="r+", shape=tuple(shape))
+
+
+def _pool_quantize(unit):
+    import oracle
+    t, i, pos, n = unit
+    x = oracle.pseudo_gradient(_POOL["th"][pos:pos + n], _POOL["tl"][i, pos:pos + n])
+    q = oracle.quantize_tensor(x)
+    _POOL["codes"][i, pos:pos + n] = q["codes"]
+    _POOL["cb"][i, t] = q["codebook"]
+    return 0
+
+
+def _pool_merge(unit):
+    import oracle
+    t, pos, n, learners, w_hat, lr, beta = unit
+    g = oracle.merge([_POOL["codes"][i, pos:pos + n] for i in learners], [_POOL["cb"][i, t] for i in learners],
+                     [w_hat[i] for i in learners])
+    th, mo = oracle.nesterov(_POOL["th"][pos:pos + n], _POOL["mo"][pos:pos + n], g, lr, beta)
+    _POOL["th_out"][pos:pos + n] = th
+    _POOL["mo_out"][pos:pos + n] = mo
+    return 0
+
+
+def cpu_baseline_parallel(res, budget_params=48_000_000, max_workers=16, check=False):
+    """The oracle's functions over a process pool, on host copies of mid-size
+    tensors of the same workload (each at most a quarter of the sample, so the
+    units balance).  check=True also returns the pool's theta and momentum with
+    the sample's tensor list, for comparison with oracle.outer_step."""
+    import multiprocessing as mp
+    import tempfile
+    import numpy as np
+    import oracle
+    inp = res["inp"]
+    k = inp.theta_L.shape[0]
+    learners = [i for i in range(k) if inp.present[i]]
+    chosen, total = [], 0
+    for t, (o, lo, n) in sorted(enumerate(inp.tensors), key=lambda x: -x[1][2]):
+        if n > budget_params // 4 or total + n > budget_params:
+            continue
+        chosen.append(t)
+        total += n
+    if not chosen:
+        return None
+    stride = sum((inp.tensors[t][2] + 63) // 64 * 64 for t in chosen)
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    with tempfile.TemporaryDirectory() as tmp:
+        spec = {"th": ([stride], "float32"), "mo": ([stride], "float32"), "tl": ([k, stride], "float32"),
+                "codes": ([k, stride], "uint8"), "cb": ([k, len(chosen), 256], "float32"),
+                "th_out": ([stride], "float32"), "mo_out": ([stride], "float32")}
+        spec = {name: (os.path.join(tmp, name), shape, dt) for name, (shape, dt) in spec.items()}
+        arr = {name: np.memmap(path, dtype=dt, mode="w+", shape=tuple(shape)) for name, (path, shape, dt) in spec.items()}
+        units_q, units_m, pos = [], [], 0
+        w_hat = oracle.normalize_weights(inp.weights)
+        for j, t in enumerate(chosen):
+            o, lo, n = inp.tensors[t]
+            arr["th"][pos:pos + n] = inp.theta_g[o:o + n].cpu().numpy()
+            arr["mo"][pos:pos + n] = inp.momentum[o:o + n].cpu().numpy()
+            for i in learners:
+                arr["tl"][i, pos:pos + n] = inp.theta_L[i, lo:lo + n].cpu().numpy()
+                units_q.append((j, i, pos, n))
+            units_m.append((j, pos, n, learners, w_hat, res["cfg"].lr, res["cfg"].beta))
+            pos += (n + 63) // 64 * 64
+        for a in arr.values():
+            a.flush()
+        ctx = mp.get_context("spawn")
+        with ctx.Pool(workers, initializer=_pool_attach, initargs=(spec,)) as pool:
+            pool.map(_pool_attach, [spec] * workers)  # workers up and attached before the clock starts
+            t0 = time.perf_counter()
+            units_q.sort(key=lambda u: -u[3])
+            pool.map(_pool_quantize, units_q, chunksize=1)
+            pool.map(_pool_merge, units_m, chunksize=1)
+            dt = time.perf_counter() - t0
+        if check:
+            sel, pos = [], 0
+            for t in chosen:
+                sel.append((t, pos))
+                pos += (inp.tensors[t][2] + 63) // 64 * 64
+            return dict(theta=np.array(arr["th_out"]), momentum=np.array(arr["mo_out"]), tensors=sel)
+    kp = len(learners)
+    return dict(value=total / dt, unit="params/s", cores=workers, kind="oracle",
+                gbps=total * (24 + 10 * kp) / dt / 1e9,
+                sample=f"{len(chosen)} mid-size tensors of the workload ({total} params, K={kp}): "
+                       f"oracle.quantize_tensor per (tensor, learner), then oracle.merge + oracle.nesterov "
+                       f"per tensor, on a pool of {workers} spawned processes; {dt:.2f} s",
+                seconds=dt)
 
 
 def cpu_model():
@@ -230,6 +464,9 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_probe:
         print(json.dumps({"copy_probe": copy_probe(device)}))
+        return
+    if args.reported:
+        print(json.dumps({"reported": reported(device, args.reported_only)}), flush=True)
         return
     copy = copy_probe(device)
     print(f"# copy ceiling {copy['gbps']:.0f} GB/s", file=sys.stderr, flush=True)

@@ -74,7 +74,9 @@ Partition make_partition(const dlc_tensor* t, int32_t n, int64_t max_tiles, int6
       g.t[i].count = (uint32_t)d.numel;
       g.t[i].block_first = (int32_t)blocks;
       const int64_t tiles = (d.numel + dlc::kTile - 1) / dlc::kTile;
-      blocks += (tiles + tpb - 1) / tpb;
+      const int64_t nb = (tiles + tpb - 1) / tpb;
+      blocks += nb;
+      g.hist_slices = std::max<int32_t>(g.hist_slices, (int32_t)((nb + dlc::kHistSlice - 1) / dlc::kHistSlice));
     }
     g.n_blocks = (int32_t)blocks;
     p.n_slots += blocks;
@@ -99,17 +101,20 @@ Partition merge_partition(const dlc_tensor* t, int32_t n) {
 }
 
 struct WorkspaceLayout {
-  size_t stats = 0, hist = 0, total = 0;
+  size_t stats = 0, hist = 0, hist_sum = 0, total = 0;
 };
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Workspace: per-block statistics partials, then per-block packed histograms.
-WorkspaceLayout workspace_layout(int64_t stats_slots, int64_t hist_slots, int32_t n_learners) {
+// Workspace: per-block statistics partials, per-block packed histograms, then
+// the histogram slice entries (at most slots / kHistSlice + tensors + 2).
+WorkspaceLayout workspace_layout(int64_t stats_slots, int64_t hist_slots, int32_t n_tensors, int32_t n_learners) {
   WorkspaceLayout w;
   w.stats = 0;
   w.hist = round256((size_t)stats_slots * (size_t)n_learners * sizeof(double) * 2);
-  w.total = w.hist + round256((size_t)hist_slots * (size_t)n_learners * dlc::kBuckets * sizeof(uint64_t));
+  w.hist_sum = w.hist + round256((size_t)hist_slots * (size_t)n_learners * dlc::kBuckets * sizeof(uint64_t));
+  const size_t entries = (size_t)(hist_slots / dlc::kHistSlice) + (size_t)n_tensors + 2;
+  w.total = w.hist_sum + round256(entries * (size_t)n_learners * dlc::kBuckets * 2 * sizeof(uint64_t));
   return w;
 }
 
@@ -174,7 +179,7 @@ int32_t setup_quant(Common& c, const float* theta_global, const float* theta_lea
   if (kp == 0) return fail(DLC_ERR_NO_QUORUM, "no learner is present");
   c.part_stats = stats_partition(tensors, n_tensors);
   c.part_enc = encode_partition(tensors, n_tensors);
-  const WorkspaceLayout wl = workspace_layout(c.part_stats.n_slots, c.part_enc.n_slots, kp);
+  const WorkspaceLayout wl = workspace_layout(c.part_stats.n_slots, c.part_enc.n_slots, n_tensors, kp);
   if (workspace == nullptr || workspace_bytes < wl.total)
     return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(wl.total) + " bytes");
   if (!aligned256(workspace)) return fail(DLC_ERR_ALIGNMENT, "workspace must be 256-byte aligned");
@@ -185,6 +190,7 @@ int32_t setup_quant(Common& c, const float* theta_global, const float* theta_lea
   c.args.n_present = kp;
   c.args.part_stats = reinterpret_cast<double2*>(ws + wl.stats);
   c.args.part_hist = reinterpret_cast<uint64_t*>(ws + wl.hist);
+  c.args.hist_sum = reinterpret_cast<uint64_t*>(ws + wl.hist_sum);
   c.stream = static_cast<hipStream_t>(hip_stream);
   return DLC_OK;
 }
@@ -219,7 +225,9 @@ int32_t run_encode(Common& c) {
       hipError_t e = dlc::launch_encode(c.args, g, c.stream);
       if (e != hipSuccess) return hip_fail(e, "encode kernel launch");
     }
-    hipError_t e = dlc::launch_codebook(c.args, g, c.stream);
+    hipError_t e = dlc::launch_hist_reduce(c.args, g, c.stream);
+    if (e != hipSuccess) return hip_fail(e, "histogram reduction kernel launch");
+    e = dlc::launch_codebook(c.args, g, c.stream);
     if (e != hipSuccess) return hip_fail(e, "codebook kernel launch");
   }
   return DLC_OK;
@@ -260,7 +268,7 @@ int32_t dlc_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32
   if (rc != DLC_OK) return rc;
   const Partition ps = stats_partition(tensors, n_tensors);
   const Partition pe = encode_partition(tensors, n_tensors);
-  *bytes = workspace_layout(ps.n_slots, pe.n_slots, n_learners).total;
+  *bytes = workspace_layout(ps.n_slots, pe.n_slots, n_tensors, n_learners).total;
   return ok();
 }
 

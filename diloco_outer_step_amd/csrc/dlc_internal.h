@@ -29,6 +29,10 @@ constexpr int kLearnerChunk = 16;         // learners per encode launch
 // kMaxEncodeTiles tiles of a tensor (2^17 elements per learner), so neither field
 // can overflow: 2^17 * 2^27 <= 2^44 and 2^17 < 2^20.
 constexpr int kMaxEncodeTiles = 32;
+// The codebook stage sums a tensor's block histograms in slices of kHistSlice
+// blocks (unpacked: 64 * 2^17 elements keep the count within 2^23 and the
+// position sum within 2^50), then the slices.
+constexpr int kHistSlice = 64;
 constexpr int kHistFracBits = 26;
 constexpr int kHistBias = 1 << 13;
 constexpr int kHistCountShift = 44;
@@ -56,6 +60,7 @@ struct LaunchGeom {
   int32_t n_blocks;         // blocks in this launch
   int32_t tiles_per_block;
   int32_t slot_base;        // workspace slot of block 0
+  int32_t hist_slices;      // most histogram slices of one tensor in this launch (encode partition)
   TensorDesc t[kMaxTensorsPerLaunch];
 };
 
@@ -72,6 +77,7 @@ struct QuantArgs {
   float* codebook;          // [n_learners][n_tensors_call][256]
   double2* part_stats;      // [slot][n_present] {sum(d), sum(d^2)}, d = Delta - shift
   uint64_t* part_hist;      // [slot][n_present][256] packed (count, position sum)
+  uint64_t* hist_sum;       // [slice entry][n_present][256][2] {position sum, count}, see hist_entry
 };
 
 struct MergeArgs {
@@ -91,6 +97,7 @@ struct MergeArgs {
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
+hipError_t launch_hist_reduce(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
 

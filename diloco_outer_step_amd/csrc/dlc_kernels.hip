@@ -250,36 +250,40 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
 }
 
 // ---------------------------------------------------------------------------
-// k_range: one thread per (present learner, tensor of the launch).  The tensor's
-// block partials are summed in block order (deterministic); loads are issued
-// eight at a time ahead of the dependent adds.
+// k_range: one block per (present learner, tensor of the launch).  Thread j sums
+// the tensor's block partials j, j + kRangeThreads, ... in that order, then a
+// fixed pairwise tree combines the threads: deterministic for a given partition.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void k_range(const QuantArgs a, const LaunchGeom g) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= a.n_present * g.n_tensors) return;
-  const int k = idx / g.n_tensors;
-  const int t = idx - k * g.n_tensors;
+constexpr int kRangeThreads = 256;
+
+__global__ __launch_bounds__(kRangeThreads) void k_range(const QuantArgs a, const LaunchGeom g) {
+  __shared__ double r1[kRangeThreads], r2[kRangeThreads];
+  const int k = blockIdx.x / g.n_tensors;
+  const int t = blockIdx.x - k * g.n_tensors;
+  const int j = threadIdx.x;
   const TensorDesc td = g.t[t];
-  const int b0 = td.block_first, b1 = tensor_block_end(g, t);
+  const int b0 = td.block_first, nb = tensor_block_end(g, t) - b0;
   const double2* p = a.part_stats + (size_t)(g.slot_base + b0) * a.n_present + k;
-  const int nb = b1 - b0;
   double S1 = 0.0, S2 = 0.0;
-  int b = 0;
-  for (; b + 8 <= nb; b += 8) {
-    double2 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(b + u) * a.n_present];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      S1 += v[u].x;
-      S2 += v[u].y;
-    }
-  }
-  for (; b < nb; ++b) {
+  for (int b = j; b < nb; b += kRangeThreads) {
     const double2 v = p[(size_t)b * a.n_present];
     S1 += v.x;
     S2 += v.y;
   }
+  r1[j] = S1;
+  r2[j] = S2;
+  __syncthreads();
+#pragma unroll
+  for (int h = kRangeThreads / 2; h > 0; h >>= 1) {
+    if (j < h) {
+      r1[j] += r1[j + h];
+      r2[j] += r2[j + h];
+    }
+    __syncthreads();
+  }
+  if (j != 0) return;
+  S1 = r1[0];
+  S2 = r2[0];
   const int li = a.learner[k];
   const float g0 = a.theta_g[td.offset()];
   const float l0 = a.theta_L[(int64_t)li * a.stride + td.loffset()];
@@ -587,47 +591,58 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
 }
 
 // ---------------------------------------------------------------------------
-// k_codebook: one block of 1024 threads per (present learner, tensor).  Thread
-// (g, c) sums bucket c over every fourth block partial of the tensor (integer, so
-// the order does not matter), the four groups combine in LDS, then
-//   cb[c] = fl32(lo + wd * (c + Q / (n * 2^s)))
-// with n the bucket count and Q the sum of the element positions q; an empty
-// bucket holds its midpoint fl32(lo + (c + 1/2) wd).
+// The codebook stage, in two kernels.  k_hist_reduce: one block per (histogram
+// slice, present learner, tensor): 4 groups of 256 threads (one per bucket) sum
+// every fourth block histogram of the slice's kHistSlice blocks, unpacked to
+// (position sum, count), combine in LDS and write one slice entry.  k_codebook:
+// one block of 256 threads per (present learner, tensor) sums the tensor's slice
+// entries and forms
+//   cb[c] = fl32(lo + wd * (c + (Q / n + f) / 2^s))
+// with n the bucket count, Q the sum of the element positions (bias removed) and
+// f the origin fraction of EncodePar; an empty bucket holds its midpoint
+// fl32(lo + (c + 1/2) wd).  Every sum is an integer sum, so the order does not
+// matter.
+// Slice entry of slice s of tensor t: floor(first global slot / kHistSlice) +
+// global tensor index + s.  Distinct tensors never share an entry, and a call
+// needs at most slots / kHistSlice + tensors + 2 entries.
 // ---------------------------------------------------------------------------
 constexpr int kCodebookGroups = 4;
 
-__global__ __launch_bounds__(kBuckets * kCodebookGroups) void k_codebook(const QuantArgs a, const LaunchGeom g) {
-  __shared__ int64_t sq[kCodebookGroups][kBuckets];
+__device__ __forceinline__ size_t hist_entry(const LaunchGeom& g, int t, int s) {
+  return (size_t)((g.slot_base + g.t[t].block_first) / kHistSlice) + (size_t)(g.t_base + t) + (size_t)s;
+}
+
+__global__ __launch_bounds__(kBuckets * kCodebookGroups) void k_hist_reduce(const QuantArgs a, const LaunchGeom g) {
+  __shared__ uint64_t sq[kCodebookGroups][kBuckets];
   __shared__ uint64_t sn[kCodebookGroups][kBuckets];
-  const int k = blockIdx.x / g.n_tensors;
-  const int t = blockIdx.x - k * g.n_tensors;
+  const int sl = blockIdx.x;
+  const int k = blockIdx.y / g.n_tensors;
+  const int t = blockIdx.y - k * g.n_tensors;
+  const int b0 = g.t[t].block_first, nb = tensor_block_end(g, t) - b0;
+  const int first = sl * kHistSlice;
+  if (first >= nb) return;
+  const int count = nb - first < kHistSlice ? nb - first : kHistSlice;
   const int c = threadIdx.x & (kBuckets - 1);
   const int grp = threadIdx.x >> 8;
-  const int li = a.learner[k];
-  const size_t row = (size_t)li * g.n_tensors_call + g.t_base + t;
-  const float4 r = a.range[row];
-  const int b0 = g.t[t].block_first, b1 = tensor_block_end(g, t);
   const size_t step = (size_t)a.n_present * kBuckets;
-  const uint64_t* p = a.part_hist + ((size_t)(g.slot_base + b0) * a.n_present + k) * kBuckets + c;
-  int64_t Q = 0;
-  uint64_t N = 0;
+  const uint64_t* p = a.part_hist + ((size_t)(g.slot_base + b0 + first) * a.n_present + k) * kBuckets + c;
+  uint64_t Q = 0, N = 0;
+  constexpr uint64_t kSumMask = (1ull << kHistCountShift) - 1;
   int b = grp;
-  for (; b + 7 * kCodebookGroups < b1 - b0; b += 8 * kCodebookGroups) {
-    uint64_t v[8];
+  for (; b + 3 * kCodebookGroups < count; b += 4 * kCodebookGroups) {
+    uint64_t v[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[(size_t)(b + u * kCodebookGroups) * step];
+    for (int u = 0; u < 4; ++u) v[u] = p[(size_t)(b + u * kCodebookGroups) * step];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint64_t n = v[u] >> kHistCountShift;
-      N += n;
-      Q += (int64_t)(v[u] & ((1ull << kHistCountShift) - 1)) - (int64_t)n * kHistBias;
+    for (int u = 0; u < 4; ++u) {
+      N += v[u] >> kHistCountShift;
+      Q += v[u] & kSumMask;
     }
   }
-  for (; b < b1 - b0; b += kCodebookGroups) {
+  for (; b < count; b += kCodebookGroups) {
     const uint64_t v = p[(size_t)b * step];
-    const uint64_t n = v >> kHistCountShift;
-    N += n;
-    Q += (int64_t)(v & ((1ull << kHistCountShift) - 1)) - (int64_t)n * kHistBias;
+    N += v >> kHistCountShift;
+    Q += v & kSumMask;
   }
   sq[grp][c] = Q;
   sn[grp][c] = N;
@@ -637,10 +652,31 @@ __global__ __launch_bounds__(kBuckets * kCodebookGroups) void k_codebook(const Q
     Q += sq[u][c];
     N += sn[u][c];
   }
+  uint64_t* e = a.hist_sum + ((hist_entry(g, t, sl) * a.n_present + k) * kBuckets + c) * 2;
+  e[0] = Q;
+  e[1] = N;
+}
+
+__global__ __launch_bounds__(kBuckets) void k_codebook(const QuantArgs a, const LaunchGeom g) {
+  const int k = blockIdx.x / g.n_tensors;
+  const int t = blockIdx.x - k * g.n_tensors;
+  const int c = threadIdx.x;
+  const int li = a.learner[k];
+  const size_t row = (size_t)li * g.n_tensors_call + g.t_base + t;
+  const float4 r = a.range[row];
+  const int nb = tensor_block_end(g, t) - g.t[t].block_first;
+  const int slices = (nb + kHistSlice - 1) / kHistSlice;
+  uint64_t Qb = 0, N = 0;
+  for (int sl = 0; sl < slices; ++sl) {
+    const uint64_t* e = a.hist_sum + ((hist_entry(g, t, sl) * a.n_present + k) * kBuckets + c) * 2;
+    Qb += e[0];
+    N += e[1];
+  }
   float out;
   if (!(r.z >= FLT_MIN)) {
     out = r.w;
   } else if (N > 0) {
+    const int64_t Q = (int64_t)(Qb - N * (uint64_t)kHistBias);
     const EncodePar par = make_encode_par(r);
     const double frac = ((double)Q / (double)N + par.origin_frac) / -par.neg_two_s;
     out = (float)((double)r.x + (double)r.z * ((double)c + frac));
@@ -855,8 +891,7 @@ hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) 
 }
 
 hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
-  const int n = a.n_present * g.n_tensors;
-  hipLaunchKernelGGL(k_range, dim3((n + 63) / 64), dim3(64), 0, s, a, g);
+  hipLaunchKernelGGL(k_range, dim3(a.n_present * g.n_tensors), dim3(kRangeThreads), 0, s, a, g);
   return hipGetLastError();
 }
 
@@ -887,8 +922,14 @@ hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s)
   return launch_encode_r<1>(a, g, s);
 }
 
+hipError_t launch_hist_reduce(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
+  hipLaunchKernelGGL(k_hist_reduce, dim3(g.hist_slices, a.n_present * g.n_tensors), dim3(kBuckets * kCodebookGroups),
+                     0, s, a, g);
+  return hipGetLastError();
+}
+
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
-  hipLaunchKernelGGL(k_codebook, dim3(a.n_present * g.n_tensors), dim3(kBuckets * kCodebookGroups), 0, s, a, g);
+  hipLaunchKernelGGL(k_codebook, dim3(a.n_present * g.n_tensors), dim3(kBuckets), 0, s, a, g);
   return hipGetLastError();
 }
 

@@ -1,0 +1,23 @@
+"""Host-side pieces of bench.py that need no GPU: the process-pool run of the
+oracle used for the CPU baseline reproduces oracle.outer_step exactly."""
+import numpy as np
+
+import bench
+import oracle
+import workloads
+
+
+def test_pool_oracle_equals_outer_step():
+    cfg = workloads.custom("pool", [3000, 64 * 1000 + 17, 5000, 40000], 3, delta="student_t",
+                           weights="dirichlet")
+    ids = list(range(4))
+    inp = workloads.fragment_inputs(cfg, ids, "cpu")
+    res = dict(inp=inp, cfg=cfg, k_present=3, bytes_per_param=54)
+    got = bench.cpu_baseline_parallel(res, budget_params=300_000, max_workers=3, check=True)
+    ref = oracle.outer_step(inp.theta_g.numpy(), inp.momentum.numpy(), inp.theta_L.numpy(), inp.theta_L.shape[1],
+                            inp.tensors, inp.weights, inp.present, cfg.lr, cfg.beta)
+    assert len(got["tensors"]) == 4
+    for t, pos in got["tensors"]:
+        o, _, n = inp.tensors[t]
+        np.testing.assert_array_equal(got["theta"][pos:pos + n], ref["theta"][o:o + n])
+        np.testing.assert_array_equal(got["momentum"][pos:pos + n], ref["momentum"][o:o + n])
