@@ -183,8 +183,10 @@ class FragmentCall:
 
 
 def time_calls(calls, reps, warmup, before=None):
-    """Median ms of each call over reps rounds (events on the launch stream); the
-    optional `before` runs untimed ahead of every call."""
+    """Median ms of each call over reps rounds, with events on the launch stream
+    between consecutive calls; the calls of a round are enqueued back to back and
+    synchronized once per round.  The optional `before` runs untimed ahead of
+    every call (then each call is timed on its own)."""
     import statistics
     import torch
     stream = torch.cuda.current_stream()
@@ -193,17 +195,20 @@ def time_calls(calls, reps, warmup, before=None):
             c()
     torch.cuda.synchronize()
     ms = [[] for _ in calls]
+    rounds = []
     for _ in range(reps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(calls))]
         for j, c in enumerate(calls):
             if before is not None:
                 before()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            ev[2 * j].record(stream)
             c()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms[j].append(e0.elapsed_time(e1))
-    return [statistics.median(m) for m in ms]
+            ev[2 * j + 1].record(stream)
+        torch.cuda.synchronize()
+        for j in range(len(calls)):
+            ms[j].append(ev[2 * j].elapsed_time(ev[2 * j + 1]))
+        rounds.append(ev[0].elapsed_time(ev[-1]))
+    return [statistics.median(m) for m in ms], statistics.median(rounds)
 
 
 def fragment_cycle(key, device, reps=5, warmup=2):
@@ -221,7 +226,7 @@ def fragment_cycle(key, device, reps=5, warmup=2):
         codes = torch.empty(inp.theta_L.shape, dtype=torch.uint8, device=device)
         calls = [FragmentCall(inp, [t for t in ids if frag[t] == p], theta, mom, codes, cfg.lr, cfg.beta)
                  for p in range(cfg.n_fragments) if any(f == p for f in frag)]
-        ms = time_calls(calls, reps, warmup)
+        ms, cycle_ms = time_calls(calls, reps, warmup)
         for c, m in zip(calls, ms):
             per.append(m)
             total_params += c.n_params
@@ -237,12 +242,13 @@ def fragment_cycle(key, device, reps=5, warmup=2):
             theta, mom = inp.theta_g.clone(), inp.momentum.clone()
             codes = torch.empty(inp.theta_L.shape, dtype=torch.uint8, device=device)
             c = FragmentCall(inp, list(range(len(sel))), theta, mom, codes, cfg.lr, cfg.beta)
-            per.append(time_calls([c], reps, warmup)[0])
+            per.append(time_calls([c], reps, warmup)[0][0])
             total_params += c.n_params
             total_bytes += (24 + 10 * c.k_present) * c.n_params
             del c, inp, theta, mom, codes
             torch.cuda.empty_cache()
-    cycle_ms = sum(per)
+    if cfg.absent_p != 0.0:
+        cycle_ms = sum(per)  # fragments built one at a time: the sum of their medians
     return dict(workload=cfg.title, fragments=len(per), cycle_ms=cycle_ms, fragment_ms=per,
                 params=total_params, params_per_s=total_params / (cycle_ms * 1e-3),
                 hbm_gbps=total_bytes / (cycle_ms * 1e-3) / 1e9,
@@ -261,7 +267,7 @@ def single_call_cold(key, device, reps=20, warmup=3, scratch_bytes=512 << 20):
     codes = torch.empty(inp.theta_L.shape, dtype=torch.uint8, device=device)
     c = FragmentCall(inp, ids, theta, mom, codes, cfg.lr, cfg.beta)
     scratch = torch.empty(scratch_bytes // 4, dtype=torch.float32, device=device)
-    ms = time_calls([c], reps, warmup, before=lambda: scratch.fill_(1.0))[0]
+    ms = time_calls([c], reps, warmup, before=lambda: scratch.fill_(1.0))[0][0]
     b = (24 + 10 * c.k_present) * c.n_params
     return dict(workload=cfg.title, ms=ms, params=c.n_params, params_per_s=c.n_params / (ms * 1e-3),
                 hbm_gbps=b / (ms * 1e-3) / 1e9, hbm_frac=b / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,

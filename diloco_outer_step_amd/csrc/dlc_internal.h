@@ -97,7 +97,7 @@ struct MergeArgs {
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
-hipError_t launch_hist_reduce(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
+// histogram slices, then the codebook (one kernel when every tensor has one slice)
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
 

@@ -612,6 +612,28 @@ __device__ __forceinline__ size_t hist_entry(const LaunchGeom& g, int t, int s) 
   return (size_t)((g.slot_base + g.t[t].block_first) / kHistSlice) + (size_t)(g.t_base + t) + (size_t)s;
 }
 
+// Codebook entry c of (present learner k, tensor t) from its bucket totals.
+__device__ __forceinline__ void write_codebook(const QuantArgs& a, const LaunchGeom& g, int k, int t, int c,
+                                               uint64_t Qb, uint64_t N) {
+  const size_t row = (size_t)a.learner[k] * g.n_tensors_call + g.t_base + t;
+  const float4 r = a.range[row];
+  float out;
+  if (!(r.z >= FLT_MIN)) {
+    out = r.w;
+  } else if (N > 0) {
+    const int64_t Q = (int64_t)(Qb - N * (uint64_t)kHistBias);
+    const EncodePar par = make_encode_par(r);
+    const double frac = ((double)Q / (double)N + par.origin_frac) / -par.neg_two_s;
+    out = (float)((double)r.x + (double)r.z * ((double)c + frac));
+  } else {
+    out = (float)((double)r.x + ((double)c + 0.5) * (double)r.z);
+  }
+  a.codebook[row * kBuckets + c] = out;
+}
+
+// FINAL: every tensor of the launch has a single slice; write the codebook
+// directly instead of a slice entry.
+template <bool FINAL>
 __global__ __launch_bounds__(kBuckets * kCodebookGroups) void k_hist_reduce(const QuantArgs a, const LaunchGeom g) {
   __shared__ uint64_t sq[kCodebookGroups][kBuckets];
   __shared__ uint64_t sn[kCodebookGroups][kBuckets];
@@ -652,18 +674,19 @@ __global__ __launch_bounds__(kBuckets * kCodebookGroups) void k_hist_reduce(cons
     Q += sq[u][c];
     N += sn[u][c];
   }
-  uint64_t* e = a.hist_sum + ((hist_entry(g, t, sl) * a.n_present + k) * kBuckets + c) * 2;
-  e[0] = Q;
-  e[1] = N;
+  if (FINAL) {
+    write_codebook(a, g, k, t, c, Q, N);
+  } else {
+    uint64_t* e = a.hist_sum + ((hist_entry(g, t, sl) * a.n_present + k) * kBuckets + c) * 2;
+    e[0] = Q;
+    e[1] = N;
+  }
 }
 
 __global__ __launch_bounds__(kBuckets) void k_codebook(const QuantArgs a, const LaunchGeom g) {
   const int k = blockIdx.x / g.n_tensors;
   const int t = blockIdx.x - k * g.n_tensors;
   const int c = threadIdx.x;
-  const int li = a.learner[k];
-  const size_t row = (size_t)li * g.n_tensors_call + g.t_base + t;
-  const float4 r = a.range[row];
   const int nb = tensor_block_end(g, t) - g.t[t].block_first;
   const int slices = (nb + kHistSlice - 1) / kHistSlice;
   uint64_t Qb = 0, N = 0;
@@ -672,18 +695,7 @@ __global__ __launch_bounds__(kBuckets) void k_codebook(const QuantArgs a, const 
     Qb += e[0];
     N += e[1];
   }
-  float out;
-  if (!(r.z >= FLT_MIN)) {
-    out = r.w;
-  } else if (N > 0) {
-    const int64_t Q = (int64_t)(Qb - N * (uint64_t)kHistBias);
-    const EncodePar par = make_encode_par(r);
-    const double frac = ((double)Q / (double)N + par.origin_frac) / -par.neg_two_s;
-    out = (float)((double)r.x + (double)r.z * ((double)c + frac));
-  } else {
-    out = (float)((double)r.x + ((double)c + 0.5) * (double)r.z);
-  }
-  a.codebook[row * kBuckets + c] = out;
+  write_codebook(a, g, k, t, c, Qb, N);
 }
 
 // ---------------------------------------------------------------------------
@@ -922,13 +934,15 @@ hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s)
   return launch_encode_r<1>(a, g, s);
 }
 
-hipError_t launch_hist_reduce(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
-  hipLaunchKernelGGL(k_hist_reduce, dim3(g.hist_slices, a.n_present * g.n_tensors), dim3(kBuckets * kCodebookGroups),
-                     0, s, a, g);
-  return hipGetLastError();
-}
-
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
+  const dim3 grid(g.hist_slices, a.n_present * g.n_tensors), block(kBuckets * kCodebookGroups);
+  if (g.hist_slices == 1) {
+    hipLaunchKernelGGL(k_hist_reduce<true>, grid, block, 0, s, a, g);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_hist_reduce<false>, grid, block, 0, s, a, g);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_codebook, dim3(a.n_present * g.n_tensors), dim3(kBuckets), 0, s, a, g);
   return hipGetLastError();
 }
