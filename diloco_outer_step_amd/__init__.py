@@ -24,6 +24,7 @@ DLC_ERR_NO_QUORUM = -3
 DLC_ERR_WORKSPACE = -4
 DLC_ERR_HIP = -5
 DLC_RANGE_GIVEN = 1
+DLC_BROADCAST = 2
 DLC_MAX_LEARNERS = 64
 DLC_N_BUCKETS = 256
 DLC_ALIGN_ELEMS = 64
@@ -31,7 +32,8 @@ DLC_RANGE_FIELDS = 4
 
 EXPORTED = (
     "dlc_fragment_plan", "dlc_workspace_bytes", "dlc_quantize_range", "dlc_quantize_encode",
-    "dlc_quantize", "dlc_merge_outer_step", "dlc_last_error", "dlc_version",
+    "dlc_quantize", "dlc_merge_outer_step", "dlc_broadcast", "dlc_cycle_workspace_bytes", "dlc_outer_cycle",
+    "dlc_last_error", "dlc_version",
 )
 
 
@@ -63,6 +65,10 @@ def _load() -> ctypes.CDLL:
         "dlc_quantize": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, u32, vp, sz, vp],
         "dlc_merge_outer_step": [vp, vp, vp, i64, i32, vp, vp, tp, i32, ctypes.c_double,
                                  ctypes.c_double, u32, vp],
+        "dlc_broadcast": [vp, vp, i64, i32, vp, tp, i32, vp],
+        "dlc_cycle_workspace_bytes": [i32, tp, vp, i32, ctypes.POINTER(sz)],
+        "dlc_outer_cycle": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, ctypes.c_double, ctypes.c_double,
+                            u32, vp, sz, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -188,6 +194,57 @@ def dlc_merge_outer_step(theta_g, momentum, codes, codebook, weights, tensors, l
     _check(_lib.dlc_merge_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(codes), codes.shape[1], k,
                                      _ptr(codebook), ctypes.cast(w, ctypes.c_void_p), arr, n, float(lr),
                                      float(beta), 0, _stream(stream)))
+
+
+def dlc_broadcast(theta_g, theta_L, tensors, rows=None, stream=None):
+    """Copy each tensor's theta_g into the learner rows of theta_L (all rows, or
+    those with rows[i] true)."""
+    k = theta_L.shape[0]
+    arr, n = _tensors(tensors)
+    _buf, sel = _present(rows, k)
+    _check(_lib.dlc_broadcast(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, sel, arr, n,
+                              _stream(stream)))
+
+
+def _fragments(fragment_first: Sequence[int]):
+    buf = (ctypes.c_int32 * len(fragment_first))(*[int(v) for v in fragment_first])
+    return buf, ctypes.cast(buf, ctypes.c_void_p)
+
+
+def group_by_fragment(tensors, fragment_of, n_fragments):
+    """Tensors reordered fragment by fragment (stable) -> (tensors, fragment_first,
+    order), where order[j] is the original index of the j-th tensor."""
+    order = sorted(range(len(tensors)), key=lambda t: (fragment_of[t], t))
+    first = [0] * (n_fragments + 1)
+    for t in order:
+        first[fragment_of[t] + 1] += 1
+    for f in range(n_fragments):
+        first[f + 1] += first[f]
+    return [tensors[t] for t in order], first, order
+
+
+def dlc_cycle_workspace_bytes(n_learners: int, tensors, fragment_first) -> int:
+    arr, _ = _tensors(tensors)
+    _fb, fp = _fragments(fragment_first)
+    out = ctypes.c_size_t(0)
+    _check(_lib.dlc_cycle_workspace_bytes(int(n_learners), arr, fp, len(fragment_first) - 1, ctypes.byref(out)))
+    return out.value
+
+
+def dlc_outer_cycle(theta_g, momentum, theta_L, tensors, fragment_first, weights, codes, codebook, range_out,
+                    workspace, lr=0.7, beta=0.9, broadcast=False, quantize_stream=None, merge_stream=None):
+    """One outer step over every fragment; weights is [n_fragments][n_learners]."""
+    k = theta_L.shape[0]
+    nf = len(fragment_first) - 1
+    arr, _ = _tensors(tensors)
+    _fb, fp = _fragments(fragment_first)
+    w = (ctypes.c_double * (nf * k))(*[float(x) for row in weights for x in row])
+    qs = _stream(quantize_stream)
+    ms = qs if merge_stream is None else _stream(merge_stream)
+    _check(_lib.dlc_outer_cycle(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k,
+                                ctypes.cast(w, ctypes.c_void_p), arr, fp, nf, _ptr(codes), _ptr(codebook),
+                                _ptr(range_out), float(lr), float(beta), DLC_BROADCAST if broadcast else 0,
+                                _ptr(workspace), workspace.numel(), qs, ms))
 
 
 def outputs_for(n_learners: int, learner_stride: int, n_tensors: int, device="cuda"):

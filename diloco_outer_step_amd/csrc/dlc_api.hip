@@ -35,6 +35,7 @@ int32_t ok() {
 constexpr int64_t kStatsBlocks = 4096;
 constexpr int64_t kEncodeBlocks = 8192;
 constexpr int64_t kMergeBlocks = 16384;
+constexpr int64_t kBroadcastBlocks = 8192;
 // At least one full group of 4 tiles per statistics or encode block: on a
 // single 4096^2 tensor, 4-tile blocks ran the step 27% faster than 1-tile blocks
 // (per-block setup, histogram flush and pipeline start amortized); large sets
@@ -93,6 +94,15 @@ Partition make_partition(const dlc_tensor* t, int32_t n, int64_t max_tiles, int6
 
 constexpr int64_t kUnlimitedTiles = int64_t(1) << 40;
 
+// Range / codebook rows for a call that is one fragment of a cycle: its tensors
+// are rows row_base.. of tables with rows_total rows per learner.
+void set_rows(Partition& p, int32_t row_base, int32_t rows_total) {
+  for (dlc::LaunchGeom& g : p.launches) {
+    g.row_base = row_base;
+    g.n_tensors_call = rows_total;
+  }
+}
+
 // The block partition of each pass.  The workspace holds one statistics slot per
 // statistics block and one histogram slot per encode block.
 Partition stats_partition(const dlc_tensor* t, int32_t n) {
@@ -101,6 +111,10 @@ Partition stats_partition(const dlc_tensor* t, int32_t n) {
 
 Partition encode_partition(const dlc_tensor* t, int32_t n) {
   return make_partition(t, n, dlc::kMaxEncodeTiles, kEncodeBlocks, 1, kEncodeMinTiles);
+}
+
+Partition broadcast_partition(const dlc_tensor* t, int32_t n) {
+  return make_partition(t, n, kUnlimitedTiles, kBroadcastBlocks);
 }
 
 // merge blocks work on kMergeTiles tiles side by side
@@ -171,7 +185,7 @@ struct Common {
 int32_t setup_quant(Common& c, const float* theta_global, const float* theta_learners,
                     int64_t learner_stride, int32_t n_learners, const uint8_t* present,
                     const dlc_tensor* tensors, int32_t n_tensors, void* workspace,
-                    size_t workspace_bytes, void* hip_stream) {
+                    size_t workspace_bytes, void* hip_stream, int32_t row_base = 0, int32_t rows_total = -1) {
   if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
     return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
   if (!theta_global || !theta_learners) return fail(DLC_ERR_INVALID_ARGUMENT, "theta pointer is NULL");
@@ -187,6 +201,10 @@ int32_t setup_quant(Common& c, const float* theta_global, const float* theta_lea
   if (kp == 0) return fail(DLC_ERR_NO_QUORUM, "no learner is present");
   c.part_stats = stats_partition(tensors, n_tensors);
   c.part_enc = encode_partition(tensors, n_tensors);
+  if (rows_total >= 0) {
+    set_rows(c.part_stats, row_base, rows_total);
+    set_rows(c.part_enc, row_base, rows_total);
+  }
   const WorkspaceLayout wl = workspace_layout(c.part_stats.n_slots, c.part_enc.n_slots, n_tensors, kp);
   if (workspace == nullptr || workspace_bytes < wl.total)
     return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(wl.total) + " bytes");
@@ -236,6 +254,87 @@ int32_t run_encode(Common& c) {
     hipError_t e = dlc::launch_codebook(c.args, g, c.stream);
     if (e != hipSuccess) return hip_fail(e, "codebook kernel launch");
   }
+  return DLC_OK;
+}
+
+// Merge arguments: checks and fp64 weight normalization (left-to-right sum).
+int32_t prepare_merge(dlc::MergeArgs& a, float* theta_global, float* momentum, const uint8_t* codes,
+                      int64_t learner_stride, int32_t n_learners, const float* codebook, const double* weights,
+                      double lr, double beta) {
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  if (!theta_global || !momentum || !codes || !codebook || !weights)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "theta_global, momentum, codes, codebook and weights must not be NULL");
+  if (!aligned256(theta_global) || !aligned256(momentum) || !aligned256(codes) || !aligned256(codebook))
+    return fail(DLC_ERR_ALIGNMENT, "device pointers must be 256-byte aligned");
+  if (!std::isfinite(lr) || !std::isfinite(beta)) return fail(DLC_ERR_INVALID_ARGUMENT, "lr and beta must be finite");
+  double total = 0.0;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (!(weights[i] >= 0.0) || !std::isfinite(weights[i]))
+      return fail(DLC_ERR_INVALID_ARGUMENT, "weights must be finite and >= 0");
+    total += weights[i];
+  }
+  if (!(total > 0.0)) return fail(DLC_ERR_NO_QUORUM, "all learner weights are zero (no quorum)");
+  std::memset(&a, 0, sizeof(a));
+  int32_t kp = 0;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (weights[i] > 0.0) {
+      a.learner[kp] = i;
+      a.w_hat[kp] = weights[i] / total;
+      ++kp;
+    }
+  }
+  a.theta_g = theta_global;
+  a.momentum = momentum;
+  a.codes = codes;
+  a.codebook = codebook;
+  a.stride = learner_stride;
+  a.n_present = kp;
+  a.lr = lr;
+  a.beta = beta;
+  return DLC_OK;
+}
+
+int32_t run_merge(const dlc::MergeArgs& a, const dlc_tensor* tensors, int32_t n_tensors, int32_t row_base,
+                  int32_t rows_total, hipStream_t s) {
+  Partition p = merge_partition(tensors, n_tensors);
+  if (rows_total >= 0) set_rows(p, row_base, rows_total);
+  for (const dlc::LaunchGeom& g : p.launches) {
+    hipError_t e = dlc::launch_merge(a, g, s);
+    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+  }
+  return DLC_OK;
+}
+
+int32_t run_broadcast(const float* theta_global, float* theta_learners, int64_t learner_stride, int32_t n_learners,
+                      const uint8_t* rows, const dlc_tensor* tensors, int32_t n_tensors, hipStream_t s) {
+  dlc::BroadcastArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.theta_g = theta_global;
+  a.theta_L = theta_learners;
+  a.stride = learner_stride;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (rows == nullptr || rows[i] != 0) a.row[a.n_rows++] = i;
+  }
+  if (a.n_rows == 0) return DLC_OK;
+  const Partition p = broadcast_partition(tensors, n_tensors);
+  for (const dlc::LaunchGeom& g : p.launches) {
+    hipError_t e = dlc::launch_broadcast(a, g, s);
+    if (e != hipSuccess) return hip_fail(e, "broadcast kernel launch");
+  }
+  return DLC_OK;
+}
+
+// fragment_first: n_fragments + 1 nondecreasing offsets from 0, at least one tensor.
+int32_t check_fragments(const dlc_tensor* tensors, const int32_t* fragment_first, int32_t n_fragments) {
+  if (!tensors || !fragment_first) return fail(DLC_ERR_INVALID_ARGUMENT, "tensors and fragment_first must not be NULL");
+  if (n_fragments < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "n_fragments must be >= 1");
+  if (fragment_first[0] != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "fragment_first[0] must be 0");
+  for (int32_t f = 0; f < n_fragments; ++f) {
+    if (fragment_first[f + 1] < fragment_first[f])
+      return fail(DLC_ERR_INVALID_ARGUMENT, "fragment_first must be nondecreasing");
+  }
+  if (fragment_first[n_fragments] < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "the fragments hold no tensor");
   return DLC_OK;
 }
 
@@ -341,47 +440,117 @@ int32_t dlc_merge_outer_step(float* theta_global, float* momentum, const uint8_t
                              const double* weights, const dlc_tensor* tensors, int32_t n_tensors,
                              double lr, double beta, uint32_t flags, void* hip_stream) {
   if (flags != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "flags must be 0");
+  dlc::MergeArgs a;
+  int32_t rc = prepare_merge(a, theta_global, momentum, codes, learner_stride, n_learners, codebook, weights, lr, beta);
+  if (rc != DLC_OK) return rc;
+  rc = check_tensors(tensors, n_tensors, learner_stride, true);
+  if (rc != DLC_OK) return rc;
+  rc = run_merge(a, tensors, n_tensors, 0, -1, static_cast<hipStream_t>(hip_stream));
+  return rc == DLC_OK ? ok() : rc;
+}
+
+int32_t dlc_broadcast(const float* theta_global, float* theta_learners, int64_t learner_stride,
+                      int32_t n_learners, const uint8_t* rows, const dlc_tensor* tensors, int32_t n_tensors,
+                      void* hip_stream) {
   if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
     return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
-  if (!theta_global || !momentum || !codes || !codebook || !weights)
-    return fail(DLC_ERR_INVALID_ARGUMENT, "theta_global, momentum, codes, codebook and weights must not be NULL");
-  if (!aligned256(theta_global) || !aligned256(momentum) || !aligned256(codes) || !aligned256(codebook))
-    return fail(DLC_ERR_ALIGNMENT, "device pointers must be 256-byte aligned");
-  if (!std::isfinite(lr) || !std::isfinite(beta)) return fail(DLC_ERR_INVALID_ARGUMENT, "lr and beta must be finite");
+  if (!theta_global || !theta_learners) return fail(DLC_ERR_INVALID_ARGUMENT, "theta pointer is NULL");
+  if (!aligned256(theta_global) || !aligned256(theta_learners))
+    return fail(DLC_ERR_ALIGNMENT, "theta pointers must be 256-byte aligned");
   int32_t rc = check_tensors(tensors, n_tensors, learner_stride, true);
   if (rc != DLC_OK) return rc;
-  // Normalize in fp64 with a left-to-right sum over all learners.
-  double total = 0.0;
-  for (int32_t i = 0; i < n_learners; ++i) {
-    if (!(weights[i] >= 0.0) || !std::isfinite(weights[i]))
-      return fail(DLC_ERR_INVALID_ARGUMENT, "weights must be finite and >= 0");
-    total += weights[i];
+  rc = run_broadcast(theta_global, theta_learners, learner_stride, n_learners, rows, tensors, n_tensors,
+                     static_cast<hipStream_t>(hip_stream));
+  return rc == DLC_OK ? ok() : rc;
+}
+
+int32_t dlc_cycle_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, const int32_t* fragment_first,
+                                  int32_t n_fragments, size_t* bytes) {
+  if (!bytes) return fail(DLC_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  int32_t rc = check_fragments(tensors, fragment_first, n_fragments);
+  if (rc != DLC_OK) return rc;
+  size_t most = 0;
+  for (int32_t f = 0; f < n_fragments; ++f) {
+    const int32_t n = fragment_first[f + 1] - fragment_first[f];
+    if (n == 0) continue;
+    const dlc_tensor* t = tensors + fragment_first[f];
+    rc = check_tensors(t, n, 0, false);
+    if (rc != DLC_OK) return rc;
+    const Partition ps = stats_partition(t, n);
+    const Partition pe = encode_partition(t, n);
+    most = std::max(most, workspace_layout(ps.n_slots, pe.n_slots, n, n_learners).total);
   }
-  if (!(total > 0.0)) return fail(DLC_ERR_NO_QUORUM, "all learner weights are zero (no quorum)");
-  dlc::MergeArgs a;
-  std::memset(&a, 0, sizeof(a));
-  int32_t kp = 0;
-  for (int32_t i = 0; i < n_learners; ++i) {
-    if (weights[i] > 0.0) {
-      a.learner[kp] = i;
-      a.w_hat[kp] = weights[i] / total;
-      ++kp;
+  *bytes = most;
+  return ok();
+}
+
+int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learners, int64_t learner_stride,
+                        int32_t n_learners, const double* weights, const dlc_tensor* tensors,
+                        const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
+                        float* range, double lr, double beta, uint32_t flags, void* workspace,
+                        size_t workspace_bytes, void* quantize_stream, void* merge_stream) {
+  if ((flags & ~DLC_BROADCAST) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
+  if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
+  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
+    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
+  int32_t rc = check_fragments(tensors, fragment_first, n_fragments);
+  if (rc != DLC_OK) return rc;
+  const int32_t n_tensors = fragment_first[n_fragments];
+  rc = check_tensors(tensors, n_tensors, learner_stride, true);
+  if (rc != DLC_OK) return rc;
+  if (!weights) return fail(DLC_ERR_INVALID_ARGUMENT, "weights is NULL");
+  // Every check before anything is enqueued: per-fragment merge arguments and quorum,
+  // quantize setup (workspace size) for every non-empty fragment.
+  std::vector<dlc::MergeArgs> margs(n_fragments);
+  std::vector<Common> qc(n_fragments);
+  std::vector<uint8_t> present(n_learners);
+  for (int32_t f = 0; f < n_fragments; ++f) {
+    const int32_t n = fragment_first[f + 1] - fragment_first[f];
+    if (n == 0) continue;
+    const double* w = weights + (size_t)f * n_learners;
+    rc = prepare_merge(margs[f], theta_global, momentum, codes, learner_stride, n_learners, codebook, w, lr, beta);
+    if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
+    for (int32_t i = 0; i < n_learners; ++i) present[i] = w[i] > 0.0 ? 1 : 0;
+    rc = setup_quant(qc[f], theta_global, theta_learners, learner_stride, n_learners, present.data(),
+                     tensors + fragment_first[f], n, workspace, workspace_bytes, quantize_stream, fragment_first[f],
+                     n_tensors);
+    if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
+    qc[f].args.range = reinterpret_cast<float4*>(range);
+    qc[f].args.codes = codes;
+    qc[f].args.codebook = codebook;
+  }
+  hipStream_t qs = static_cast<hipStream_t>(quantize_stream), ms = static_cast<hipStream_t>(merge_stream);
+  for (int32_t f = 0; f < n_fragments; ++f) {
+    const int32_t n = fragment_first[f + 1] - fragment_first[f];
+    if (n == 0) continue;
+    rc = run_range(qc[f]);
+    if (rc == DLC_OK) rc = run_encode(qc[f]);
+    if (rc != DLC_OK) return rc;
+    // merge of this fragment after its quantization; the next fragment's
+    // quantization proceeds on the quantize stream meanwhile
+    hipEvent_t done;
+    hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(done, qs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ms, done, 0);
+    if (e == hipSuccess) e = hipEventDestroy(done);
+    if (e != hipSuccess) return hip_fail(e, "cycle event");
+    rc = run_merge(margs[f], tensors + fragment_first[f], n, fragment_first[f], n_tensors, ms);
+    if (rc != DLC_OK) return rc;
+    if (flags & DLC_BROADCAST) {
+      rc = run_broadcast(theta_global, theta_learners, learner_stride, n_learners, nullptr,
+                         tensors + fragment_first[f], n, ms);
+      if (rc != DLC_OK) return rc;
     }
   }
-  a.theta_g = theta_global;
-  a.momentum = momentum;
-  a.codes = codes;
-  a.codebook = codebook;
-  a.stride = learner_stride;
-  a.n_present = kp;
-  a.lr = lr;
-  a.beta = beta;
-  const Partition p = merge_partition(tensors, n_tensors);
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  for (const dlc::LaunchGeom& g : p.launches) {
-    hipError_t e = dlc::launch_merge(a, g, s);
-    if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
-  }
+  // the quantize stream joins the merge stream: either stream completes the cycle
+  hipEvent_t end;
+  hipError_t e = hipEventCreateWithFlags(&end, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(end, ms);
+  if (e == hipSuccess) e = hipStreamWaitEvent(qs, end, 0);
+  if (e == hipSuccess) e = hipEventDestroy(end);
+  if (e != hipSuccess) return hip_fail(e, "cycle event");
   return ok();
 }
 

@@ -56,7 +56,8 @@ struct TensorDesc {
 struct LaunchGeom {
   int32_t n_tensors;        // tensors in this launch
   int32_t t_base;           // call-level index of the launch's first tensor
-  int32_t n_tensors_call;   // tensors in the whole call (row length of range / codebook)
+  int32_t n_tensors_call;   // row length of range / codebook
+  int32_t row_base;         // range / codebook row of the call's first tensor (0 unless part of a cycle)
   int32_t n_blocks;         // blocks in this launch
   int32_t tiles_per_block;
   int32_t slot_base;        // workspace slot of block 0
@@ -93,6 +94,14 @@ struct MergeArgs {
   double beta;
 };
 
+struct BroadcastArgs {
+  const float* theta_g;
+  float* theta_L;
+  int64_t stride;
+  int32_t n_rows;                 // learner rows written
+  int32_t row[kMaxLearners];      // their learner indices
+};
+
 // Kernel launchers (dlc_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
@@ -100,5 +109,6 @@ hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s)
 // histogram slices, then the codebook (one kernel when every tensor has one slice)
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
+hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStream_t s);
 
 }  // namespace dlc

@@ -299,7 +299,7 @@ __global__ __launch_bounds__(kRangeThreads) void k_range(const QuantArgs a, cons
   r.y = (float)(mu + 6.0 * sigma);
   r.z = (float)(12.0 * sigma / 256.0);
   r.w = (float)mu;
-  a.range[(size_t)li * g.n_tensors_call + g.t_base + t] = r;
+  a.range[(size_t)li * g.n_tensors_call + g.row_base + g.t_base + t] = r;
 }
 
 // ---------------------------------------------------------------------------
@@ -491,7 +491,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
 
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
-  const size_t rrow = (size_t)g.t_base + sp.t;
+  const size_t rrow = (size_t)g.row_base + g.t_base + sp.t;
   for (int i = tid; i < kc * R * kBuckets; i += kBlock) hist[i] = 0;
   if (tid < kc) par[tid] = make_encode_par(a.range[(size_t)a.learner[a.k_base + tid] * g.n_tensors_call + rrow]);
   __syncthreads();
@@ -615,7 +615,7 @@ __device__ __forceinline__ size_t hist_entry(const LaunchGeom& g, int t, int s) 
 // Codebook entry c of (present learner k, tensor t) from its bucket totals.
 __device__ __forceinline__ void write_codebook(const QuantArgs& a, const LaunchGeom& g, int k, int t, int c,
                                                uint64_t Qb, uint64_t N) {
-  const size_t row = (size_t)a.learner[k] * g.n_tensors_call + g.t_base + t;
+  const size_t row = (size_t)a.learner[k] * g.n_tensors_call + g.row_base + g.t_base + t;
   const float4 r = a.range[row];
   float out;
   if (!(r.z >= FLT_MIN)) {
@@ -772,7 +772,7 @@ __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))
   const int kp = a.n_present;
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
-  const size_t trow = (size_t)g.t_base + sp.t;
+  const size_t trow = (size_t)g.row_base + g.t_base + sp.t;
 
   for (int i = threadIdx.x; i < kp * kBuckets; i += kMergeBlock) {
     const int k = i >> 8, c = i & (kBuckets - 1);
@@ -877,6 +877,73 @@ __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_broadcast: the updated theta_g of each tensor copied into every given learner
+// row.  A full tile of theta_g is loaded once (the next one is requested before
+// the current one is stored) and stored to each row as one 16 KB run of
+// non-temporal stores; tiles past the block's full tiles, and rows past n_rows,
+// are null requests and dropped stores.  NR > 0: rows padded to NR at compile
+// time, so every tile issues the same sequence of memory operations (the
+// prologue adds one tile's worth of null stores); NR = 0: any number of rows.
+// The partial tail tile is copied element by element.
+// ---------------------------------------------------------------------------
+constexpr int kBroadcastMaxRows = 16;
+
+template <int NR>
+__global__ __launch_bounds__(kBlock) void k_broadcast(const BroadcastArgs a, const LaunchGeom g) {
+  const int tid = threadIdx.x;
+  const Span sp = block_span(g);
+  const TensorDesc td = g.t[sp.t];
+  const float* __restrict__ src = a.theta_g + td.offset() + sp.begin;
+  const int64_t n_full = (sp.end - sp.begin) / kTile;
+  auto row_of = [&](int r) { return a.theta_L + (int64_t)a.row[r] * a.stride + td.loffset() + sp.begin; };
+  if (n_full > 0) {
+    const int rows = NR > 0 ? NR : a.n_rows;
+    auto request = [&](float (&dst)[kVec], int64_t tile) {
+      const bool valid = tile < n_full;
+      load_tile_rsrc(tile_rsrc(src + (valid ? tile : 0) * kTile, valid), tid, dst);
+    };
+    auto store_rows = [&](const float (&v)[kVec], int64_t tile) {
+      constexpr int kUnroll = NR > 0 ? NR : 1;
+#pragma unroll kUnroll
+      for (int r = 0; r < rows; ++r) {
+        const bool valid = tile < n_full && r < a.n_rows;
+        float* dst = row_of(r < a.n_rows ? r : 0) + (valid ? tile : 0) * kTile;
+        store_tile_rsrc(tile_rsrc(dst, valid), tid, v);
+      }
+    };
+    float v0[kVec], v1[kVec];
+    request(v0, 0);
+    if (NR > 0) {
+      const float zero[kVec] = {};
+      store_rows(zero, n_full);  // null stores: the steady state's previous tile
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t i = 0; i < n_full; i += 2) {
+      request(v1, i + 1);
+      store_rows(v0, i);
+      request(v0, i + 2);
+      store_rows(v1, i + 1);
+    }
+  }
+  const int64_t full_len = n_full * kTile;
+  if (sp.begin + full_len < sp.end) {
+    const int64_t n = sp.end - sp.begin - full_len;
+    float v[kVec];
+    load_tail(src + full_len, tid, n, v);
+    for (int r = 0; r < a.n_rows; ++r) {
+      float* dst = row_of(r) + full_len;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (tail_valid(tid, j, c, n)) dst[elem_index(tid, j, c)] = v[4 * j + c];
+        }
+      }
+    }
+  }
+}
+
 template <typename K>
 hipError_t allow_lds(K kernel, size_t lds) {
   if (lds <= 65536) return hipSuccess;
@@ -965,6 +1032,19 @@ hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) 
     case 4: return launch_merge_r<4>(a, g, s);
     default: return launch_merge_r<0>(a, g, s);
   }
+}
+
+hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStream_t s) {
+  static_assert(kBroadcastMaxRows == 16, "one instantiation per padded row count");
+  const dim3 grid(g.n_blocks), block(kBlock);
+  switch ((a.n_rows + 3) / 4) {
+    case 1: hipLaunchKernelGGL(k_broadcast<4>, grid, block, 0, s, a, g); break;
+    case 2: hipLaunchKernelGGL(k_broadcast<8>, grid, block, 0, s, a, g); break;
+    case 3: hipLaunchKernelGGL(k_broadcast<12>, grid, block, 0, s, a, g); break;
+    case 4: hipLaunchKernelGGL(k_broadcast<16>, grid, block, 0, s, a, g); break;
+    default: hipLaunchKernelGGL(k_broadcast<0>, grid, block, 0, s, a, g); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace dlc

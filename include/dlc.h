@@ -63,6 +63,9 @@ extern "C" {
 
 /* dlc_quantize flag: use the caller's `range` instead of computing it. */
 #define DLC_RANGE_GIVEN 1u
+/* dlc_outer_cycle flag: after each fragment's merge, copy its updated theta into
+   every learner replica (dlc_broadcast). */
+#define DLC_BROADCAST 2u
 
 #define DLC_MAX_LEARNERS 64
 #define DLC_N_BUCKETS 256
@@ -172,6 +175,57 @@ int32_t dlc_merge_outer_step(float* theta_global, float* momentum, const uint8_t
                              int64_t learner_stride, int32_t n_learners, const float* codebook,
                              const double* weights, const dlc_tensor* tensors, int32_t n_tensors,
                              double lr, double beta, uint32_t flags, void* hip_stream);
+
+/*
+ * dlc_broadcast -- send the updated fragment back to the learners (INTELLECT-1
+ * notes, section 3.2 step 8: every worker copies the updated weights before the
+ * next outer step; Decoupled DiLoCo digest, "architecture": the syncer sends the
+ * updated fragment back).  For every tensor and every learner i with rows[i] != 0
+ * (rows NULL = all n_learners):
+ *   theta_learners[i][loffset .. loffset + numel) = theta_global[offset .. offset + numel)
+ * bit for bit.  theta_learners is written only there.  Same layout, alignment and
+ * stream rules as the other calls.
+ */
+int32_t dlc_broadcast(const float* theta_global, float* theta_learners, int64_t learner_stride,
+                      int32_t n_learners, const uint8_t* rows, const dlc_tensor* tensors, int32_t n_tensors,
+                      void* hip_stream);
+
+/*
+ * dlc_outer_cycle -- one outer step over every fragment of a model, fragments in
+ * id order (Decoupled DiLoCo digest, "architecture" item 4: P fragments merged one
+ * at a time; the quantization of fragment p + 1 overlaps the merge of fragment p,
+ * as the learners' and the syncer's work overlap with tau = 2 there).
+ *   tensors         all tensors, grouped by fragment: fragment f owns
+ *                   tensors[fragment_first[f] .. fragment_first[f + 1]) (may be empty)
+ *   fragment_first  host int32 [n_fragments + 1], nondecreasing, fragment_first[0] = 0,
+ *                   fragment_first[n_fragments] = number of tensors >= 1
+ *   weights         host double [n_fragments][n_learners]: raw weights of each
+ *                   fragment's merge; 0 = learner absent for that fragment (not
+ *                   read, not quantized).  Every non-empty fragment needs a
+ *                   positive total (else DLC_ERR_NO_QUORUM, nothing enqueued).
+ *   codes           device uint8 [n_learners][learner_stride]
+ *   codebook        device fp32 [n_learners][n_tensors][256], row = global tensor index
+ *   range           device fp32 [n_learners][n_tensors][4], row = global tensor index
+ *   flags           0 or DLC_BROADCAST
+ *   workspace       >= dlc_cycle_workspace_bytes(...) bytes
+ *   quantize_stream the quantize calls (dlc_quantize of each fragment);
+ *   merge_stream    the merge (and broadcast) calls; each waits for its fragment's
+ *                   quantization on the other stream through an event.  Both may
+ *                   be the same stream.  At the end the quantize stream waits for
+ *                   the merge stream, so synchronizing either completes the cycle.
+ * Results are those of calling dlc_quantize, dlc_merge_outer_step (and
+ * dlc_broadcast) fragment by fragment.  Per-call events are created and
+ * destroyed inside the call.  All argument errors, including every fragment's
+ * quorum and workspace size, are returned before anything is enqueued.
+ */
+int32_t dlc_cycle_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, const int32_t* fragment_first,
+                                  int32_t n_fragments, size_t* bytes);
+
+int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learners, int64_t learner_stride,
+                        int32_t n_learners, const double* weights, const dlc_tensor* tensors,
+                        const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
+                        float* range, double lr, double beta, uint32_t flags, void* workspace,
+                        size_t workspace_bytes, void* quantize_stream, void* merge_stream);
 
 /* Message of the last error on the calling thread ("" if none). */
 const char* dlc_last_error(void);

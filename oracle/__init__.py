@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, by the package smoke check and
 by the benchmark's cpu_baseline leg, never by the product path.
 """
 from .core import (  # noqa: F401
-    CLIP_SIGMAS, FLT_MIN, N_BUCKETS, NoQuorum, clip_range, clip_values, codebook,
+    CLIP_SIGMAS, FLT_MIN, N_BUCKETS, NoQuorum, broadcast, clip_range, clip_values, codebook,
     dequantize, encode, fragment_plan, histogram, merge, nesterov, normalize_weights,
-    outer_step, pseudo_gradient, quantize_tensor, tensor_stats,
+    outer_cycle, outer_step, pseudo_gradient, quantize_tensor, tensor_stats,
 )

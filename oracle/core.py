@@ -25,6 +25,10 @@ bucket index.  Sources (the pages):
         bin-packing of whole tensors into balanced fragments (note 1);
       - section "fault tolerance", items 1 and 3: merge once a minimum quorum
         has arrived; learners are weighted (token/step weighted merge).
+      - section "architecture": the syncer holds the global fragments, merges
+        one fragment at a time and sends the updated fragment back; the
+        INTELLECT-1 notes' section 3.2 step 8 likewise has every worker copy the
+        updated weights before the next outer step (broadcast, outer_cycle).
 
 Readings taken where the pages are silent (each also listed in the design doc):
   * sigma is the population std (ddof = 0) of the whole tensor;
@@ -257,3 +261,44 @@ def outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights,
         gs[t] = g
         th[off:off + n], mom[off:off + n] = nesterov(tg, mom[off:off + n], g, lr, beta)
     return dict(theta=th, momentum=mom, quant=quant, g=gs)
+
+
+# ---------------------------------------------------------------------------
+# Sending the update back, and a whole outer step over every fragment.
+# ---------------------------------------------------------------------------
+def broadcast(theta_g, theta_L, tensors, rows=None):
+    """Every learner copies the updated tensors (INTELLECT-1 notes, section 3.2
+    step 8; Decoupled DiLoCo digest, "architecture": the syncer sends the updated
+    fragment back).  Returns a new [K, stride] array; rows selects learners."""
+    out = np.array(theta_L, dtype=np.float32, copy=True)
+    for off, loff, n in tensors:
+        for i in range(out.shape[0]):
+            if rows is None or rows[i]:
+                out[i, loff:loff + n] = theta_g[off:off + n]
+    return out
+
+
+def outer_cycle(theta_g, momentum, theta_L, learner_stride, tensors, fragment_first, weights,
+                lr=0.7, beta=0.9, send_back=False):
+    """One outer step over every fragment in id order (Decoupled DiLoCo digest,
+    "architecture" item 4).  Fragment f owns tensors[fragment_first[f]:
+    fragment_first[f + 1]] and merges with weights[f] (0 = learner absent for
+    that fragment).  With send_back, the fragment's updated tensors are copied to
+    every learner right after its merge.  Returns dict(theta, momentum, theta_L,
+    steps={f: outer_step result})."""
+    th = np.array(theta_g, dtype=np.float32, copy=True)
+    mom = np.array(momentum, dtype=np.float32, copy=True)
+    tl = np.array(theta_L, dtype=np.float32, copy=True)
+    steps = {}
+    for f in range(len(fragment_first) - 1):
+        sel = list(tensors[fragment_first[f]:fragment_first[f + 1]])
+        if not sel:
+            continue
+        w = list(weights[f])
+        res = outer_step(th, mom, tl, learner_stride, sel, w, [1 if x > 0 else 0 for x in w], lr, beta)
+        th, mom = res["theta"], res["momentum"]
+        steps[f] = res
+        if send_back:
+            tl = broadcast(th, tl, sel)
+    return dict(theta=th, momentum=mom, theta_L=tl, steps=steps)
+

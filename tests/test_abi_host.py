@@ -41,8 +41,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("DLC_OK", "DLC_ERR_INVALID_ARGUMENT", "DLC_ERR_ALIGNMENT", "DLC_ERR_NO_QUORUM",
                  "DLC_ERR_WORKSPACE", "DLC_ERR_HIP", "DLC_MAX_LEARNERS", "DLC_N_BUCKETS",
-                 "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS"):
-        m = re.search(rf"#define {name} \(?(-?\d+)\)?", text)
+                 "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS", "DLC_RANGE_GIVEN", "DLC_BROADCAST"):
+        m = re.search(rf"#define {name} \(?(-?\d+)u?\)?", text)
         assert m and int(m.group(1)) == getattr(dlc, name), name
 
 
@@ -96,6 +96,31 @@ def quantize(k=2, spec=((0, 0, 4096),), stride=4096, theta=FAKE, present=None, w
     return L.dlc_quantize(theta, FAKE, stride, k, pres, arr, n, codes, FAKE, FAKE, flags, ws, ws_bytes, None)
 
 
+def broadcast(k=2, spec=((0, 0, 4096),), stride=4096, theta=FAKE):
+    L = dlc._lib
+    arr, n = dlc._tensors(spec)
+    return L.dlc_broadcast(theta, FAKE, stride, k, None, arr, n, None)
+
+
+def cycle_ws(k=2, spec=((0, 0, 4096), (4096, 4096, 64)), first=(0, 1, 2)):
+    L = dlc._lib
+    arr, _ = dlc._tensors(spec)
+    fb = (ctypes.c_int32 * len(first))(*first)
+    out = ctypes.c_size_t(0)
+    return L.dlc_cycle_workspace_bytes(k, arr, ctypes.cast(fb, ctypes.c_void_p), len(first) - 1, ctypes.byref(out))
+
+
+def cycle(k=2, spec=((0, 0, 4096), (4096, 4096, 64)), first=(0, 1, 2), stride=8192,
+          weights=((1.0, 1.0), (1.0, 1.0)), flags=0, ws_bytes=1 << 30, codes=FAKE):
+    L = dlc._lib
+    arr, _ = dlc._tensors(spec)
+    fb = (ctypes.c_int32 * len(first))(*first)
+    w = (ctypes.c_double * (len(weights) * k))(*[x for row in weights for x in row])
+    return L.dlc_outer_cycle(FAKE, FAKE, FAKE, stride, k, ctypes.cast(w, ctypes.c_void_p), arr,
+                             ctypes.cast(fb, ctypes.c_void_p), len(first) - 1, codes, FAKE, FAKE, 0.7, 0.9, flags,
+                             FAKE, ws_bytes, None, None)
+
+
 def merge(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), lr=0.7, beta=0.9, flags=0, theta=FAKE):
     arr, n = tens(spec)
     w = (ctypes.c_double * k)(*weights)
@@ -129,6 +154,22 @@ def merge(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), lr=0.7, be
     (lambda: merge(flags=1), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: merge(theta=FAKE + 8), dlc.DLC_ERR_ALIGNMENT),
     (lambda: merge(k=0, weights=()), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: broadcast(k=0), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: broadcast(theta=None), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: broadcast(theta=FAKE + 4), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: broadcast(stride=100), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: broadcast(spec=((0, 0, 0),)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_ws(first=(1, 1)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_ws(first=(0, 1, 0)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_ws(first=(0, 0, 0)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_ws(first=(0,)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle(flags=4), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle(weights=((1.0, 1.0), (0.0, 0.0))), dlc.DLC_ERR_NO_QUORUM),
+    (lambda: cycle(weights=((1.0, 1.0), (1.0, -2.0))), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle(ws_bytes=64), dlc.DLC_ERR_WORKSPACE),
+    (lambda: cycle(codes=FAKE + 32), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: cycle(first=(0, 2, 1)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle(spec=((0, 0, 4096), (0, 4096, 64))), dlc.DLC_ERR_INVALID_ARGUMENT),
 ])
 def test_argument_errors(call, code):
     assert call() == code

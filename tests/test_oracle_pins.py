@@ -468,3 +468,73 @@ def test_workload_parameter_counts():
     assert len(workloads.config("c2").tensors) == 272
     assert len(workloads.config("c3").tensors) == 147
     assert len(workloads.config("c4").tensors) == 381
+
+
+# ---------------------------------------------------------------------------
+# The fragment cycle and sending the update back (Decoupled DiLoCo digest,
+# "architecture"; INTELLECT-1 notes, section 3.2 step 8).
+# ---------------------------------------------------------------------------
+def _cycle_case(seed=0, sizes=(700, 64 * 40 + 3, 4096, 100, 2048), k=3):
+    rng = np.random.default_rng(seed)
+    offs, pos = [], 0
+    for n in sizes:
+        offs.append(pos)
+        pos += (n + 63) // 64 * 64
+    theta = (rng.standard_normal(pos) * 0.02).astype(np.float32)
+    mom = (rng.standard_normal(pos) * 1e-3).astype(np.float32)
+    tl = np.zeros((k, pos), np.float32)
+    for i in range(k):
+        tl[i] = (theta - rng.standard_normal(pos) * 1e-3).astype(np.float32)
+    tensors = [(o, o, n) for o, n in zip(offs, sizes)]
+    return theta, mom, tl, pos, tensors
+
+
+def test_broadcast_copies_exactly_and_only_the_tensors():
+    theta, _, tl, stride, tensors = _cycle_case()
+    out = oracle.broadcast(theta, tl, tensors[1:3], rows=[1, 0, 1])
+    for i in range(3):
+        for t, (o, lo, n) in enumerate(tensors):
+            if t in (1, 2) and i != 1:
+                np.testing.assert_array_equal(out[i, lo:lo + n], theta[o:o + n])
+            else:
+                np.testing.assert_array_equal(out[i, lo:lo + n], tl[i, lo:lo + n])
+
+
+def test_cycle_with_one_fragment_is_outer_step():
+    theta, mom, tl, stride, tensors = _cycle_case(1)
+    w = [0.2, 0.5, 0.3]
+    cyc = oracle.outer_cycle(theta, mom, tl, stride, tensors, [0, len(tensors)], [w])
+    one = oracle.outer_step(theta, mom, tl, stride, tensors, w)
+    np.testing.assert_array_equal(cyc["theta"], one["theta"])
+    np.testing.assert_array_equal(cyc["momentum"], one["momentum"])
+
+
+def test_cycle_result_does_not_depend_on_fragment_order():
+    theta, mom, tl, stride, tensors = _cycle_case(2)
+    w = [[1.0, 1.0, 0.0], [0.3, 0.3, 0.4], [1.0, 0.0, 0.0]]
+    a = oracle.outer_cycle(theta, mom, tl, stride, tensors, [0, 2, 3, 5], w, send_back=True)
+    # the same fragments, listed in reverse order
+    rev = tensors[3:5] + tensors[2:3] + tensors[0:2]
+    b = oracle.outer_cycle(theta, mom, tl, stride, rev, [0, 2, 3, 5], w[::-1], send_back=True)
+    for key in ("theta", "momentum", "theta_L"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_after_sending_back_the_next_cycle_is_a_pure_momentum_step():
+    # Once every learner holds the merged theta, each pseudo-gradient is exactly
+    # zero: every tensor is degenerate (codes 0, codebook = mean = 0), g = 0, and
+    # Nesterov reduces to v <- beta v, theta <- theta - lr beta^2 v.
+    theta, mom, tl, stride, tensors = _cycle_case(3)
+    w = [[1.0, 2.0, 3.0], [1.0, 1.0, 1.0]]
+    first = [0, 3, 5]
+    c1 = oracle.outer_cycle(theta, mom, tl, stride, tensors, first, w, send_back=True)
+    c2 = oracle.outer_cycle(c1["theta"], c1["momentum"], c1["theta_L"], stride, tensors, first, w)
+    lr, beta = 0.7, 0.9
+    for o, _, n in tensors:
+        v = c1["momentum"][o:o + n].astype(np.float64)
+        t = c1["theta"][o:o + n].astype(np.float64)
+        np.testing.assert_array_equal(c2["momentum"][o:o + n], (beta * v).astype(np.float32))
+        np.testing.assert_array_equal(c2["theta"][o:o + n], (t - lr * (beta * (beta * v))).astype(np.float32))
+    for f, res in c2["steps"].items():
+        for q in res["quant"].values():
+            assert q["degenerate"] and not q["codes"].any()
