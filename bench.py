@@ -274,15 +274,100 @@ def single_call_cold(key, device, reps=20, warmup=3, scratch_bytes=512 << 20):
                 cold_cache=f"{scratch_bytes >> 20} MB scratch write before each call")
 
 
+def native_cycle(key, device, reps=5, warmup=2):
+    """The whole fragment cycle through dlc_outer_cycle: quantize and merge on one
+    stream, on two overlapped streams, and on two streams with the update sent
+    back to the learners (dlc_broadcast after each merge)."""
+    import statistics
+    import torch
+    import diloco_outer_step_amd as dlc
+    import workloads
+    cfg = workloads.config(key)
+    ids = list(range(len(cfg.tensors)))
+    inp = workloads.fragment_inputs(cfg, ids, device)
+    frag, _ = dlc.dlc_fragment_plan([s.numel for s in cfg.tensors], cfg.n_fragments)
+    grouped, first, _ = dlc.group_by_fragment(inp.tensors, frag, cfg.n_fragments)
+    k, stride = inp.theta_L.shape
+    weights = [list(inp.weights)] * cfg.n_fragments
+    codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), device)
+    ws = torch.empty(max(256, dlc.dlc_cycle_workspace_bytes(k, grouped, first)), dtype=torch.uint8, device=device)
+    theta, mom, theta_L = inp.theta_g.clone(), inp.momentum.clone(), inp.theta_L.clone()
+    qs = torch.cuda.current_stream()
+    ms = torch.cuda.Stream()
+    n_params = sum(n for _, _, n in grouped)
+    out = {}
+    for name, merge_stream, bc in (("one_stream", qs, False), ("two_streams", ms, False),
+                                   ("two_streams_send_back", ms, True)):
+        def run():
+            dlc.dlc_outer_cycle(theta, mom, theta_L if bc else inp.theta_L, grouped, first, weights, codes, cb, rng,
+                                ws, broadcast=bc, quantize_stream=qs, merge_stream=merge_stream)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(qs)
+            run()
+            e1.record(qs)  # the quantize stream joins the merge stream at the end of a cycle
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms_ = statistics.median(ts)
+        b = (24 + 10 * k + (4 + 4 * k if bc else 0)) * n_params
+        out[name] = dict(cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3), hbm_gbps=b / (ms_ * 1e-3) / 1e9,
+                         bytes_per_param=b // n_params)
+    out["workload"] = cfg.title
+    out["fragments"] = cfg.n_fragments
+    return out
+
+
+def broadcast_rate(key, device, reps=5, warmup=2):
+    """dlc_broadcast over every tensor of a set: 4 + 4K bytes per parameter."""
+    import statistics
+    import torch
+    import diloco_outer_step_amd as dlc
+    import workloads
+    cfg = workloads.config(key)
+    inp = workloads.fragment_inputs(cfg, list(range(len(cfg.tensors))), device)
+    k = inp.theta_L.shape[0]
+    theta_L = inp.theta_L
+    for _ in range(warmup):
+        dlc.dlc_broadcast(inp.theta_g, theta_L, inp.tensors)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dlc.dlc_broadcast(inp.theta_g, theta_L, inp.tensors)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms_ = statistics.median(ts)
+    n = sum(x for _, _, x in inp.tensors)
+    b = (4 + 4 * k) * n
+    return dict(workload=cfg.title, ms=ms_, params=n, learners=k, hbm_gbps=b / (ms_ * 1e-3) / 1e9,
+                hbm_frac=b / (ms_ * 1e-3) / 1e9 / PEAK_HBM_GBPS)
+
+
 def reported(device, only=None):
     """The parameter sets that are reported but not gated: the 4096^2 tensor (cold
     cache), and full 24-fragment cycles of the 135M set and of the edge mix."""
-    keys = only.split(",") if only else ["c1", "c2", "c5k1", "c5k16"]
+    import torch
+    keys = only.split(",") if only else ["c1", "c2", "c5k1", "c5k16", "native_c2", "native_c5k1", "broadcast_c3"]
     out = {}
     if "c1" in keys:
         out["c1"] = single_call_cold("c1", device)
         print(f"# c1 {out['c1']['ms']:.3f} ms", file=sys.stderr, flush=True)
-    for key in [k for k in keys if k != "c1"]:
+    for key in [k for k in keys if k.startswith("native_")]:
+        out[key] = native_cycle(key[len("native_"):], device)
+        torch.cuda.empty_cache()
+        print(f"# {key}: " + ", ".join(f"{n} {v['cycle_ms']:.3f} ms" for n, v in out[key].items()
+                                       if isinstance(v, dict)), file=sys.stderr, flush=True)
+    if "broadcast_c3" in keys:
+        out["broadcast_c3"] = broadcast_rate("c3", device)
+        torch.cuda.empty_cache()
+        print(f"# broadcast c3 {out['broadcast_c3']['ms']:.3f} ms", file=sys.stderr, flush=True)
+    for key in [k for k in keys if k in ("c2", "c5k1", "c5k16")]:
         out[key] = fragment_cycle(key, device)
         print(f"# {key} cycle {out[key]['cycle_ms']:.3f} ms over {out[key]['fragments']} fragments",
               file=sys.stderr, flush=True)
