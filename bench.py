@@ -349,11 +349,46 @@ def broadcast_rate(key, device, reps=5, warmup=2):
                 hbm_frac=b / (ms_ * 1e-3) / 1e9 / PEAK_HBM_GBPS)
 
 
+def stale_rate(key, device, reps=5, warmup=2):
+    """dlc_quantize_bases with the learners split between two bases (even learners
+    against theta_g, odd ones against an older copy): one pass per base, so the
+    statistics and encode passes read 4 + 4K bytes per parameter more than once
+    only for the second base (2 * 4 + 4K each)."""
+    import statistics
+    import torch
+    import diloco_outer_step_amd as dlc
+    import workloads
+    cfg = workloads.config(key)
+    inp = workloads.fragment_inputs(cfg, list(range(len(cfg.tensors))), device)
+    k, stride = inp.theta_L.shape
+    old = inp.theta_g.clone()
+    bases = [inp.theta_g if i % 2 == 0 else old for i in range(k)]
+    codes, cb, rng = dlc.outputs_for(k, stride, len(inp.tensors), device)
+    ws = dlc.alloc_workspace(k, inp.tensors, device)
+    for _ in range(warmup):
+        dlc.dlc_quantize_bases(bases, inp.theta_L, inp.tensors, codes, cb, rng, ws)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dlc.dlc_quantize_bases(bases, inp.theta_L, inp.tensors, codes, cb, rng, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms_ = statistics.median(ts)
+    n = sum(x for _, _, x in inp.tensors)
+    b = (2 * 4 + 4 * k + 2 * 4 + 5 * k) * n
+    return dict(workload=cfg.title, bases=2, ms=ms_, params=n, learners=k, hbm_gbps=b / (ms_ * 1e-3) / 1e9,
+                hbm_frac=b / (ms_ * 1e-3) / 1e9 / PEAK_HBM_GBPS)
+
+
 def reported(device, only=None):
     """The parameter sets that are reported but not gated: the 4096^2 tensor (cold
     cache), and full 24-fragment cycles of the 135M set and of the edge mix."""
     import torch
-    keys = only.split(",") if only else ["c1", "c2", "c5k1", "c5k16", "native_c2", "native_c5k1", "broadcast_c3"]
+    keys = only.split(",") if only else ["c1", "c2", "c5k1", "c5k16", "native_c2", "native_c5k1", "broadcast_c3",
+                                         "stale_c3"]
     out = {}
     if "c1" in keys:
         out["c1"] = single_call_cold("c1", device)
@@ -363,6 +398,10 @@ def reported(device, only=None):
         torch.cuda.empty_cache()
         print(f"# {key}: " + ", ".join(f"{n} {v['cycle_ms']:.3f} ms" for n, v in out[key].items()
                                        if isinstance(v, dict)), file=sys.stderr, flush=True)
+    if "stale_c3" in keys:
+        out["stale_c3"] = stale_rate("c3", device)
+        torch.cuda.empty_cache()
+        print(f"# stale quantize c3 {out['stale_c3']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if "broadcast_c3" in keys:
         out["broadcast_c3"] = broadcast_rate("c3", device)
         torch.cuda.empty_cache()

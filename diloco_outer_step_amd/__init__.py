@@ -4,7 +4,7 @@ The functions here carry the C ABI's names (include/dlc.h) and only marshal
 arguments: torch tensors supply device memory, torch's current HIP stream is the
 default stream, and every step of the computation runs in the library's kernels.
 Importing this package fails loudly if the library has not been built
-(``python -m diloco_outer_step_amd.build``).
+(``python diloco_outer_step_amd/build.py``).
 """
 from __future__ import annotations
 
@@ -32,8 +32,8 @@ DLC_RANGE_FIELDS = 4
 
 EXPORTED = (
     "dlc_fragment_plan", "dlc_workspace_bytes", "dlc_quantize_range", "dlc_quantize_encode",
-    "dlc_quantize", "dlc_merge_outer_step", "dlc_broadcast", "dlc_cycle_workspace_bytes", "dlc_outer_cycle",
-    "dlc_last_error", "dlc_version",
+    "dlc_quantize", "dlc_quantize_bases", "dlc_merge_outer_step", "dlc_merge_weights", "dlc_broadcast",
+    "dlc_cycle_workspace_bytes", "dlc_outer_cycle", "dlc_last_error", "dlc_version",
 )
 
 
@@ -53,7 +53,7 @@ class _Tensor(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m diloco_outer_step_amd.build`")
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python diloco_outer_step_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, u32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_size_t
     tp = ctypes.POINTER(_Tensor)
@@ -65,6 +65,8 @@ def _load() -> ctypes.CDLL:
         "dlc_quantize": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, u32, vp, sz, vp],
         "dlc_merge_outer_step": [vp, vp, vp, i64, i32, vp, vp, tp, i32, ctypes.c_double,
                                  ctypes.c_double, u32, vp],
+        "dlc_quantize_bases": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, vp, sz, vp],
+        "dlc_merge_weights": [i32, vp, vp, i32, ctypes.c_double, vp, vp],
         "dlc_broadcast": [vp, vp, i64, i32, vp, tp, i32, vp],
         "dlc_cycle_workspace_bytes": [i32, tp, vp, i32, ctypes.POINTER(sz)],
         "dlc_outer_cycle": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, ctypes.c_double, ctypes.c_double,
@@ -194,6 +196,34 @@ def dlc_merge_outer_step(theta_g, momentum, codes, codebook, weights, tensors, l
     _check(_lib.dlc_merge_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(codes), codes.shape[1], k,
                                      _ptr(codebook), ctypes.cast(w, ctypes.c_void_p), arr, n, float(lr),
                                      float(beta), 0, _stream(stream)))
+
+
+def dlc_quantize_bases(bases, theta_L, tensors, codes, codebook, range_out, workspace, present=None,
+                       stream=None):
+    """dlc_quantize with learner i's pseudo-gradient taken against bases[i] (a
+    device tensor laid out like theta_g)."""
+    k = theta_L.shape[0]
+    if len(bases) != k:
+        raise ValueError("one base per learner")
+    arr, n = _tensors(tensors)
+    _buf, pres = _present(present, k)
+    ptrs = (ctypes.c_void_p * k)(*[b.data_ptr() for b in bases])
+    _check(_lib.dlc_quantize_bases(ctypes.cast(ptrs, ctypes.c_void_p), _ptr(theta_L), _learner_stride(theta_L), k,
+                                   pres, arr, n, _ptr(codes), _ptr(codebook), _ptr(range_out), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
+
+
+def dlc_merge_weights(tokens, arrival, quorum: int, grace: float):
+    """-> (weights list, merge_time); raises NoQuorumError when the quorum is not met."""
+    k = len(tokens)
+    t = (ctypes.c_double * k)(*[float(x) for x in tokens])
+    a = (ctypes.c_double * k)(*[float(x) for x in arrival])
+    w = (ctypes.c_double * k)()
+    mt = ctypes.c_double(0.0)
+    _check(_lib.dlc_merge_weights(k, ctypes.cast(t, ctypes.c_void_p), ctypes.cast(a, ctypes.c_void_p), int(quorum),
+                                  float(grace), ctypes.cast(w, ctypes.c_void_p), ctypes.cast(ctypes.byref(mt),
+                                                                                          ctypes.c_void_p)))
+    return list(w), mt.value
 
 
 def dlc_broadcast(theta_g, theta_L, tensors, rows=None, stream=None):

@@ -1,6 +1,8 @@
 """Build the gfx950 shared library libdlc.so in-tree with hipcc.
 
-    python -m diloco_outer_step_amd.build
+    python diloco_outer_step_amd/build.py
+
+(run as a script: importing the package needs the library this builds)
 """
 from __future__ import annotations
 

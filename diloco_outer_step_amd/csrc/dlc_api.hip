@@ -435,6 +435,46 @@ int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
   return rc == DLC_OK ? ok() : rc;
 }
 
+int32_t dlc_quantize_bases(const float* const* bases, const float* theta_learners, int64_t learner_stride,
+                           int32_t n_learners, const uint8_t* present, const dlc_tensor* tensors,
+                           int32_t n_tensors, uint8_t* codes, float* codebook, float* range, void* workspace,
+                           size_t workspace_bytes, void* hip_stream) {
+  if (!bases) return fail(DLC_ERR_INVALID_ARGUMENT, "bases is NULL");
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
+  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
+    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
+  // learners grouped by base, groups in order of first appearance; every group
+  // checked before anything is enqueued
+  std::vector<const float*> order;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (present != nullptr && present[i] == 0) continue;
+    if (!bases[i]) return fail(DLC_ERR_INVALID_ARGUMENT, "bases[" + std::to_string(i) + "] is NULL");
+    if (std::find(order.begin(), order.end(), bases[i]) == order.end()) order.push_back(bases[i]);
+  }
+  if (order.empty()) return fail(DLC_ERR_NO_QUORUM, "no learner is present");
+  std::vector<Common> groups(order.size());
+  std::vector<uint8_t> member(n_learners);
+  for (size_t gi = 0; gi < order.size(); ++gi) {
+    for (int32_t i = 0; i < n_learners; ++i)
+      member[i] = (present == nullptr || present[i] != 0) && bases[i] == order[gi] ? 1 : 0;
+    int32_t rc = setup_quant(groups[gi], order[gi], theta_learners, learner_stride, n_learners, member.data(), tensors,
+                             n_tensors, workspace, workspace_bytes, hip_stream);
+    if (rc != DLC_OK) return rc;
+    groups[gi].args.range = reinterpret_cast<float4*>(range);
+    groups[gi].args.codes = codes;
+    groups[gi].args.codebook = codebook;
+  }
+  // one workspace: the groups run one after another on the stream
+  for (Common& c : groups) {
+    int32_t rc = run_range(c);
+    if (rc == DLC_OK) rc = run_encode(c);
+    if (rc != DLC_OK) return rc;
+  }
+  return ok();
+}
+
 int32_t dlc_merge_outer_step(float* theta_global, float* momentum, const uint8_t* codes,
                              int64_t learner_stride, int32_t n_learners, const float* codebook,
                              const double* weights, const dlc_tensor* tensors, int32_t n_tensors,
@@ -551,6 +591,42 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
   if (e == hipSuccess) e = hipStreamWaitEvent(qs, end, 0);
   if (e == hipSuccess) e = hipEventDestroy(end);
   if (e != hipSuccess) return hip_fail(e, "cycle event");
+  return ok();
+}
+
+int32_t dlc_merge_weights(int32_t n_learners, const double* tokens, const double* arrival, int32_t quorum,
+                          double grace, double* weights, double* merge_time) {
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  if (!tokens || !arrival || !weights) return fail(DLC_ERR_INVALID_ARGUMENT, "tokens, arrival and weights must not be NULL");
+  if (quorum < 1 || quorum > n_learners) return fail(DLC_ERR_INVALID_ARGUMENT, "quorum must be in [1, n_learners]");
+  if (!(grace >= 0.0) || std::isinf(grace)) return fail(DLC_ERR_INVALID_ARGUMENT, "grace must be finite and >= 0");
+  std::vector<int32_t> arrived;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (std::isfinite(arrival[i])) {
+      if (arrival[i] < 0.0) return fail(DLC_ERR_INVALID_ARGUMENT, "arrival times must be >= 0");
+      if (!(tokens[i] >= 0.0) || !std::isfinite(tokens[i]))
+        return fail(DLC_ERR_INVALID_ARGUMENT, "tokens of an arrived learner must be finite and >= 0");
+      arrived.push_back(i);
+    }
+  }
+  if ((int32_t)arrived.size() < quorum) return fail(DLC_ERR_NO_QUORUM, "fewer learners arrived than the quorum");
+  // the quorum is met when the quorum-th earliest learner arrives (ties: lower index first)
+  std::stable_sort(arrived.begin(), arrived.end(), [&](int32_t a, int32_t b) { return arrival[a] < arrival[b]; });
+  const double t_quorum = arrival[arrived[quorum - 1]];
+  const double deadline = t_quorum + grace;
+  double total = 0.0, last = t_quorum;
+  std::vector<double> w(n_learners, 0.0);
+  for (int32_t i : arrived) {
+    if (arrival[i] <= deadline) {
+      w[i] = tokens[i];
+      total += tokens[i];
+      last = std::max(last, arrival[i]);
+    }
+  }
+  if (!(total > 0.0)) return fail(DLC_ERR_NO_QUORUM, "the merged learners report no tokens");
+  std::copy(w.begin(), w.end(), weights);
+  if (merge_time) *merge_time = (int32_t)arrived.size() == n_learners && last < deadline ? last : deadline;
   return ok();
 }
 

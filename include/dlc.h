@@ -154,6 +154,25 @@ int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
                      size_t workspace_bytes, void* hip_stream);
 
 /*
+ * dlc_quantize_bases -- dlc_quantize for learners that started from different
+ * versions of the global parameters (Decoupled DiLoCo digest, "fault tolerance":
+ * learners run asynchronously and may report against an older global fragment).
+ * Learner i's pseudo-gradient is Delta_i = fl32(bases[i] - theta_i), every other
+ * step as in dlc_quantize (range computed, never given).
+ *   bases     host array [n_learners] of device pointers, each laid out like
+ *             theta_global (tensor t at its offset); learners with the same
+ *             pointer share one pass over that base.  Entries of absent learners
+ *             are not read.
+ * Learners are processed in groups of equal base, in order of first appearance,
+ * one after another on the stream with the same workspace
+ * (dlc_workspace_bytes(n_learners, ...) suffices).
+ */
+int32_t dlc_quantize_bases(const float* const* bases, const float* theta_learners, int64_t learner_stride,
+                           int32_t n_learners, const uint8_t* present, const dlc_tensor* tensors,
+                           int32_t n_tensors, uint8_t* codes, float* codebook, float* range, void* workspace,
+                           size_t workspace_bytes, void* hip_stream);
+
+/*
  * dlc_merge_outer_step -- dequantize, weighted mean, Nesterov (INTELLECT-1 notes,
  * section 3.2 steps 6-7 and section 4.2; Decoupled DiLoCo digest, "fault
  * tolerance" items 1 and 3).  Per element of every tensor:
@@ -226,6 +245,28 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
                         const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
                         float* range, double lr, double beta, uint32_t flags, void* workspace,
                         size_t workspace_bytes, void* quantize_stream, void* merge_stream);
+
+/*
+ * dlc_merge_weights -- which learners a fragment's merge takes, and their weights
+ * (Decoupled DiLoCo digest, "fault tolerance" items 1-3: merge once a minimum
+ * quorum has arrived, wait a little longer while the window has slack, weight
+ * learners by the tokens they processed).  Pure host code.
+ *   tokens      host [n_learners]: tokens each learner processed since its base
+ *   arrival     host [n_learners]: seconds after the fragment's window opened at
+ *               which the learner's update arrived; +inf or NaN = not arrived
+ *   quorum      minimum number of arrived learners, 1..n_learners
+ *   grace       seconds the merge may wait after the quorum is met (the caller's
+ *               remaining slack), finite and >= 0
+ *   weights     host out [n_learners]: tokens_i for every learner that arrived
+ *               by t_q + grace, 0 for the others, where t_q is the arrival of the
+ *               quorum-th earliest learner (ties: lower index first)
+ *   merge_time  host out (may be NULL): t_q + grace, or the last arrival if every
+ *               learner arrived before that
+ * DLC_ERR_NO_QUORUM when fewer than `quorum` learners arrived or the merged
+ * learners report zero tokens in total (weights untouched then).
+ */
+int32_t dlc_merge_weights(int32_t n_learners, const double* tokens, const double* arrival, int32_t quorum,
+                          double grace, double* weights, double* merge_time);
 
 /* Message of the last error on the calling thread ("" if none). */
 const char* dlc_last_error(void);

@@ -224,7 +224,7 @@ def nesterov(theta, momentum, g, lr=0.7, beta=0.9):
 # --- one merge call over a fragment -------------------------------------------
 
 def outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights,
-               present=None, lr=0.7, beta=0.9, given_ranges=None):
+               present=None, lr=0.7, beta=0.9, given_ranges=None, bases=None):
     """One outer step over the tensors of one fragment.
 
     theta_g, momentum : fp32 flat arrays (not modified; new copies are returned)
@@ -233,6 +233,10 @@ def outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights,
     weights           : raw learner weights; 0 = absent
     present           : learners that quantize (default: weight > 0)
     given_ranges      : optional {(i, t): (lo, hi, wd, mean32)} pinned ranges
+    bases             : optional list of K fp32 flat arrays laid out like theta_g:
+                        learner i's pseudo-gradient is taken against bases[i] (a
+                        stale learner's starting point, Decoupled DiLoCo digest,
+                        "fault tolerance"); the update is still applied to theta_g
 
     Returns dict(theta=..., momentum=..., quant={(i, t): quantize_tensor dict},
     g={t: fp64 merged pseudo-gradient}).  Raises NoQuorum when all weights are 0.
@@ -250,7 +254,8 @@ def outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights,
         for i in range(k):
             if not present[i]:
                 continue
-            x = pseudo_gradient(tg, theta_L[i, loff:loff + n])
+            base = tg if bases is None else np.asarray(bases[i], np.float32)[off:off + n]
+            x = pseudo_gradient(base, theta_L[i, loff:loff + n])
             gr = None if given_ranges is None else given_ranges.get((i, t))
             q = quantize_tensor(x, gr)
             quant[(i, t)] = q
@@ -301,4 +306,28 @@ def outer_cycle(theta_g, momentum, theta_L, learner_stride, tensors, fragment_fi
         if send_back:
             tl = broadcast(th, tl, sel)
     return dict(theta=th, momentum=mom, theta_L=tl, steps=steps)
+
+
+def merge_weights(tokens, arrival, quorum, grace):
+    """Which learners a fragment's merge takes and with what weight (Decoupled
+    DiLoCo digest, "fault tolerance" items 1-3): wait for `quorum` learners, then
+    at most `grace` seconds more, and weight every learner that made it by the
+    tokens it processed.  arrival[i] = inf (or NaN) means learner i never arrived.
+    Returns (weights, merge_time); raises NoQuorum if fewer than `quorum`
+    arrived or the merged learners processed no tokens."""
+    k = len(tokens)
+    came = [i for i in range(k) if np.isfinite(arrival[i])]
+    if len(came) < quorum:
+        raise NoQuorum(f"{len(came)} of {k} learners arrived, quorum {quorum}")
+    # the quorum-th arrival, earlier index first among equal times
+    by_time = sorted(came, key=lambda i: (arrival[i], i))
+    t_quorum = arrival[by_time[quorum - 1]]
+    deadline = t_quorum + grace
+    weights = [float(tokens[i]) if i in came and arrival[i] <= deadline else 0.0 for i in range(k)]
+    if sum(weights) <= 0.0:
+        raise NoQuorum("the merged learners processed no tokens")
+    in_time = [arrival[i] for i in came if arrival[i] <= deadline]
+    if len(came) == k and max(in_time) < deadline:
+        return weights, float(max(in_time))
+    return weights, float(deadline)
 

@@ -96,6 +96,16 @@ def quantize(k=2, spec=((0, 0, 4096),), stride=4096, theta=FAKE, present=None, w
     return L.dlc_quantize(theta, FAKE, stride, k, pres, arr, n, codes, FAKE, FAKE, flags, ws, ws_bytes, None)
 
 
+def quantize_bases(bases=(FAKE, FAKE), present=None, ws_bytes=16):
+    """ws_bytes=16 is too small, so a call that passes every other check stops at
+    the workspace check instead of launching."""
+    L = dlc._lib
+    arr, n = dlc._tensors(((0, 0, 4096),))
+    ptrs = None if bases is None else ctypes.cast((ctypes.c_void_p * 2)(*bases), ctypes.c_void_p)
+    pres = None if present is None else ctypes.cast((ctypes.c_uint8 * 2)(*present), ctypes.c_void_p)
+    return L.dlc_quantize_bases(ptrs, FAKE, 4096, 2, pres, arr, n, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+
 def broadcast(k=2, spec=((0, 0, 4096),), stride=4096, theta=FAKE):
     L = dlc._lib
     arr, n = dlc._tensors(spec)
@@ -154,6 +164,11 @@ def merge(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), lr=0.7, be
     (lambda: merge(flags=1), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: merge(theta=FAKE + 8), dlc.DLC_ERR_ALIGNMENT),
     (lambda: merge(k=0, weights=()), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize_bases(bases=None), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize_bases(bases=(FAKE, 0)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize_bases(bases=(FAKE, 0), present=(1, 0)), dlc.DLC_ERR_WORKSPACE),
+    (lambda: quantize_bases(present=(0, 0)), dlc.DLC_ERR_NO_QUORUM),
+    (lambda: quantize_bases(bases=(FAKE + 8, FAKE)), dlc.DLC_ERR_ALIGNMENT),
     (lambda: broadcast(k=0), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: broadcast(theta=None), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: broadcast(theta=FAKE + 4), dlc.DLC_ERR_ALIGNMENT),

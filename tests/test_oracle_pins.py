@@ -538,3 +538,36 @@ def test_after_sending_back_the_next_cycle_is_a_pure_momentum_step():
     for f, res in c2["steps"].items():
         for q in res["quant"].values():
             assert q["degenerate"] and not q["codes"].any()
+
+
+# ---------------------------------------------------------------------------
+# Learners reporting against older bases (Decoupled DiLoCo digest, "fault
+# tolerance": asynchronous learners).
+# ---------------------------------------------------------------------------
+def test_bases_equal_to_theta_g_change_nothing():
+    theta, mom, tl, stride, tensors = _cycle_case(4)
+    w = [0.5, 0.3, 0.2]
+    a = oracle.outer_step(theta, mom, tl, stride, tensors, w)
+    b = oracle.outer_step(theta, mom, tl, stride, tensors, w, bases=[theta, theta.copy(), theta.copy()])
+    np.testing.assert_array_equal(a["theta"], b["theta"])
+    np.testing.assert_array_equal(a["momentum"], b["momentum"])
+
+
+def test_stale_learner_without_progress_only_dilutes_the_others():
+    # Learner 2 reports against an old base it never moved away from: its
+    # pseudo-gradient is exactly zero, its codebook all zeros, so the merged
+    # g equals the other learners' merge scaled by W / (W + w_2).
+    theta, mom, tl, stride, tensors = _cycle_case(5)
+    rng = np.random.default_rng(9)
+    old = (theta + rng.standard_normal(theta.shape) * 1e-3).astype(np.float32)
+    tl = tl.copy()
+    tl[2] = old
+    w = [1.0, 3.0, 2.0]
+    with_stale = oracle.outer_step(theta, mom, tl, stride, tensors, w, bases=[theta, theta, old])
+    without = oracle.outer_step(theta, mom, tl, stride, tensors, [1.0, 3.0, 0.0])
+    for t in with_stale["g"]:
+        assert with_stale["quant"][(2, t)]["degenerate"]
+        # fp64 sums of the same terms with different weights: a few ulps of the
+        # largest term, relative where g does not cancel
+        scale = float(np.abs(without["g"][t]).max())
+        np.testing.assert_allclose(with_stale["g"][t], without["g"][t] * (4.0 / 6.0), rtol=1e-13, atol=1e-15 * scale)
