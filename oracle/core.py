@@ -331,3 +331,72 @@ def merge_weights(tokens, arrival, quorum, grace):
         return weights, float(max(in_time))
     return weights, float(deadline)
 
+
+# ---------------------------------------------------------------------------
+# The ring all-reduce with requantization at every hop (INTELLECT-1 notes,
+# section 3.2 step 6 and section 4.2): K ranks each hold a pseudo-gradient; a
+# message is quantized before it is sent, the receiver dequantizes it and adds it
+# to its own fp32 copy, so every hop quantizes a running sum afresh.
+# ---------------------------------------------------------------------------
+RING_ALIGN = 64
+
+
+def ring_chunks(n, k):
+    """Tensor of n elements cut into k chunks of whole 64-element groups, as
+    equal as possible: chunk j = [64 floor(j m / k), 64 floor((j + 1) m / k))
+    clipped to n, m = ceil(n / 64).  Chunks may be empty when m < k."""
+    m = -(-n // RING_ALIGN)
+    bounds = [min(n, RING_ALIGN * ((j * m) // k)) for j in range(k + 1)]
+    return [(bounds[j], bounds[j + 1]) for j in range(k)]
+
+
+def ring_outer_step(theta_g, momentum, theta_L, learner_stride, tensors, lr=0.7, beta=0.9, trace=None):
+    """One outer step whose K learners (every row of theta_L, equal weights)
+    average their pseudo-gradients through a ring, tensor by tensor:
+
+    reduce-scatter, K - 1 hops: at hop s rank r sends its running sum of chunk
+      (r - s) mod K, quantized (quantize_tensor on that chunk); rank r + 1 adds
+      the dequantized message to its own fp32 value of the chunk: acc = fl32(acc + deQ).
+    Rank r then holds the sum of chunk (r + 1) mod K; it divides by K in fp32
+      (mean = fl32(sum / K)) and quantizes the mean once.
+    all-gather: that message travels the ring unchanged, so every rank ends with
+      deQ(Q(mean)) for every chunk; g is that value, and Nesterov updates theta_g.
+
+    Returns dict(theta, momentum, g={t: fp32 array}, messages=[(tensor, hop,
+    sender, chunk, quantize_tensor dict)]).  trace, if a list, receives the
+    accumulator arrays after every hop."""
+    k = theta_L.shape[0]
+    th = np.array(theta_g, dtype=np.float32, copy=True)
+    mom = np.array(momentum, dtype=np.float32, copy=True)
+    gs, messages = {}, []
+    for t, (off, loff, n) in enumerate(tensors):
+        acc = [pseudo_gradient(th[off:off + n], theta_L[r, loff:loff + n]) for r in range(k)]
+        chunks = ring_chunks(n, k)
+        for s in range(k - 1):
+            sends = []
+            for r in range(k):
+                c = (r - s) % k
+                a, b = chunks[c]
+                if b > a:
+                    q = quantize_tensor(acc[r][a:b])
+                    messages.append((t, s, r, c, q))
+                    sends.append((r, c, dequantize(q["codes"], q["codebook"])))
+            for r, c, d in sends:  # every rank sends before anyone adds
+                a, b = chunks[c]
+                dst = (r + 1) % k
+                acc[dst][a:b] = np.add(acc[dst][a:b], d, dtype=np.float32)
+            if trace is not None:
+                trace.append([x.copy() for x in acc])
+        g = np.zeros(n, np.float32)
+        for r in range(k):
+            c = (r + 1) % k
+            a, b = chunks[c]
+            if b > a:
+                mean = np.divide(acc[r][a:b], np.float32(k), dtype=np.float32)
+                q = quantize_tensor(mean)
+                messages.append((t, k - 1, r, c, q))
+                g[a:b] = dequantize(q["codes"], q["codebook"])
+        gs[t] = g
+        th[off:off + n], mom[off:off + n] = nesterov(th[off:off + n], mom[off:off + n], g.astype(np.float64), lr, beta)
+    return dict(theta=th, momentum=mom, g=gs, messages=messages)
+

@@ -571,3 +571,76 @@ def test_stale_learner_without_progress_only_dilutes_the_others():
         # largest term, relative where g does not cancel
         scale = float(np.abs(without["g"][t]).max())
         np.testing.assert_allclose(with_stale["g"][t], without["g"][t] * (4.0 / 6.0), rtol=1e-13, atol=1e-15 * scale)
+
+
+# ---------------------------------------------------------------------------
+# The ring with requantization at every hop (INTELLECT-1 notes, section 3.2
+# step 6 and section 4.2).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 100, 1000, 4096 * 3 + 17])
+@pytest.mark.parametrize("k", [1, 2, 3, 8, 14])
+def test_ring_chunks_tile_the_tensor(n, k):
+    ch = oracle.ring_chunks(n, k)
+    assert len(ch) == k and ch[0][0] == 0 and ch[-1][1] == n
+    for (a, b), (c, d) in zip(ch, ch[1:]):
+        assert b == c and a <= b
+    for a, b in ch[:-1]:
+        assert a % 64 == 0 and b % 64 == 0
+    sizes = [b - a for a, b in ch]
+    assert max(sizes) - min(s for s in sizes) <= 64 + n % 64 or n < 64 * k
+
+
+def test_ring_with_one_rank_is_the_star_merge():
+    theta, mom, tl, stride, tensors = _cycle_case(6, k=1)
+    ring = oracle.ring_outer_step(theta, mom, tl, stride, tensors)
+    star = oracle.outer_step(theta, mom, tl, stride, tensors, [1.0])
+    np.testing.assert_array_equal(ring["theta"], star["theta"])
+    np.testing.assert_array_equal(ring["momentum"], star["momentum"])
+
+
+@pytest.mark.parametrize("k", [2, 3, 5])
+def test_ring_on_constant_chunks_is_the_ring_order_fp32_mean(k):
+    # Every message of a constant chunk has zero variance, so quantization is
+    # lossless; chunk c's sum is then Delta_c + Delta_{c+1} + ... + Delta_{c-1}
+    # added left to right in fp32 (the order the ring visits the ranks), and the
+    # mean fl32(sum / k).
+    n = 64 * 7 + 5
+    rng = np.random.default_rng(k)
+    theta = np.full(n, 1.0, np.float32)
+    ch = oracle.ring_chunks(n, k)
+    consts = rng.uniform(-1e-3, 1e-3, (k, k)).astype(np.float32)  # [rank, chunk]
+    tl = np.zeros((k, n + 64), np.float32)
+    for r in range(k):
+        for c, (a, b) in enumerate(ch):
+            tl[r, a:b] = np.float32(1.0) - consts[r, c]
+    delta = np.array([[np.float32(1.0) - tl[r, ch[c][0]] for c in range(k)] for r in range(k)], np.float32)
+    res = oracle.ring_outer_step(theta, np.zeros(n, np.float32), tl, n + 64, [(0, 0, n)])
+    for c, (a, b) in enumerate(ch):
+        if b == a:
+            continue
+        s = np.float32(0.0)
+        for j in range(k):
+            s = np.float32(s + delta[(c + j) % k, c]) if j else delta[c, c]
+        want = np.float32(s / np.float32(k))
+        np.testing.assert_array_equal(res["g"][0][a:b], np.full(b - a, want, np.float32))
+
+
+def test_ring_error_exceeds_the_star_and_grows_with_the_ring():
+    # Requantizing a running sum at every hop adds quantization noise each time;
+    # a star merge quantizes each pseudo-gradient once, so its error averages down
+    # as 1/sqrt(K) while the ring's does not: the ratio grows with K.
+    n = 64 * 2000
+    rng = np.random.default_rng(1)
+    theta = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    errs = {}
+    for k in (2, 8):
+        tl = np.stack([(theta - rng.standard_normal(n) * 1e-3).astype(np.float32) for _ in range(k)])
+        exact = np.mean([theta.astype(np.float64) - tl[r].astype(np.float32).astype(np.float64) for r in range(k)], 0)
+        mom = np.zeros(n, np.float32)
+        ring = oracle.ring_outer_step(theta, mom, tl, n, [(0, 0, n)])
+        star = oracle.outer_step(theta, mom, tl, n, [(0, 0, n)], [1.0] * k)
+        e_ring = float(np.sqrt(np.mean((ring["g"][0] - exact) ** 2)))
+        e_star = float(np.sqrt(np.mean((star["g"][0] - exact) ** 2)))
+        assert e_ring > e_star
+        errs[k] = e_ring / e_star
+    assert errs[8] > 1.5 * errs[2]
