@@ -33,7 +33,8 @@ DLC_RANGE_FIELDS = 4
 EXPORTED = (
     "dlc_fragment_plan", "dlc_workspace_bytes", "dlc_quantize_range", "dlc_quantize_encode",
     "dlc_quantize", "dlc_quantize_bases", "dlc_merge_outer_step", "dlc_merge_weights", "dlc_broadcast",
-    "dlc_cycle_workspace_bytes", "dlc_outer_cycle", "dlc_last_error", "dlc_version",
+    "dlc_cycle_workspace_bytes", "dlc_outer_cycle", "dlc_ring_workspace_bytes", "dlc_ring_outer_step",
+    "dlc_last_error", "dlc_version",
 )
 
 
@@ -68,6 +69,9 @@ def _load() -> ctypes.CDLL:
         "dlc_quantize_bases": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, vp, sz, vp],
         "dlc_merge_weights": [i32, vp, vp, i32, ctypes.c_double, vp, vp],
         "dlc_broadcast": [vp, vp, i64, i32, vp, tp, i32, vp],
+        "dlc_ring_workspace_bytes": [i32, tp, i32, ctypes.POINTER(sz)],
+        "dlc_ring_outer_step": [vp, vp, vp, i64, i32, tp, i32, ctypes.c_double, ctypes.c_double, vp, vp, vp, vp,
+                                vp, sz, vp],
         "dlc_cycle_workspace_bytes": [i32, tp, vp, i32, ctypes.POINTER(sz)],
         "dlc_outer_cycle": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, ctypes.c_double, ctypes.c_double,
                             u32, vp, sz, vp, vp],
@@ -224,6 +228,33 @@ def dlc_merge_weights(tokens, arrival, quorum: int, grace: float):
                                   float(grace), ctypes.cast(w, ctypes.c_void_p), ctypes.cast(ctypes.byref(mt),
                                                                                           ctypes.c_void_p)))
     return list(w), mt.value
+
+
+def dlc_ring_workspace_bytes(n_learners: int, tensors) -> int:
+    arr, n = _tensors(tensors)
+    out = ctypes.c_size_t(0)
+    _check(_lib.dlc_ring_workspace_bytes(int(n_learners), arr, n, ctypes.byref(out)))
+    return out.value
+
+
+def ring_buffers(theta_L, n_tensors: int):
+    """(accum, codes, codebook, range, workspace-size-less) buffers for dlc_ring_outer_step."""
+    k, stride = theta_L.shape
+    dev = theta_L.device
+    accum = torch.empty((k, stride), dtype=torch.float32, device=dev)
+    codes = torch.empty((k, stride), dtype=torch.uint8, device=dev)
+    codebook = torch.empty((k * n_tensors, DLC_N_BUCKETS), dtype=torch.float32, device=dev)
+    rng = torch.empty((k * n_tensors, DLC_RANGE_FIELDS), dtype=torch.float32, device=dev)
+    return accum, codes, codebook, rng
+
+
+def dlc_ring_outer_step(theta_g, momentum, theta_L, tensors, accum, codes, codebook, range_out, workspace, lr=0.7,
+                        beta=0.9, stream=None):
+    k = theta_L.shape[0]
+    arr, n = _tensors(tensors)
+    _check(_lib.dlc_ring_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k, arr, n,
+                                    float(lr), float(beta), _ptr(accum), _ptr(codes), _ptr(codebook), _ptr(range_out),
+                                    _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def dlc_broadcast(theta_g, theta_L, tensors, rows=None, stream=None):

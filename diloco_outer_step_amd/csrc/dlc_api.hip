@@ -185,11 +185,12 @@ struct Common {
 int32_t setup_quant(Common& c, const float* theta_global, const float* theta_learners,
                     int64_t learner_stride, int32_t n_learners, const uint8_t* present,
                     const dlc_tensor* tensors, int32_t n_tensors, void* workspace,
-                    size_t workspace_bytes, void* hip_stream, int32_t row_base = 0, int32_t rows_total = -1) {
+                    size_t workspace_bytes, void* hip_stream, int32_t row_base = 0, int32_t rows_total = -1,
+                    bool no_base = false) {
   if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
     return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
-  if (!theta_global || !theta_learners) return fail(DLC_ERR_INVALID_ARGUMENT, "theta pointer is NULL");
-  if (!aligned256(theta_global) || !aligned256(theta_learners))
+  if ((!theta_global && !no_base) || !theta_learners) return fail(DLC_ERR_INVALID_ARGUMENT, "theta pointer is NULL");
+  if ((theta_global && !aligned256(theta_global)) || !aligned256(theta_learners))
     return fail(DLC_ERR_ALIGNMENT, "theta pointers must be 256-byte aligned");
   int32_t rc = check_tensors(tensors, n_tensors, learner_stride, true);
   if (rc != DLC_OK) return rc;
@@ -323,6 +324,65 @@ int32_t run_broadcast(const float* theta_global, float* theta_learners, int64_t 
     if (e != hipSuccess) return hip_fail(e, "broadcast kernel launch");
   }
   return DLC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// The ring: chunks of whole 64-element groups, the messages of every hop as
+// segments of the flat [ranks][stride] accumulator and code buffers (one
+// "learner" row of ranks * stride elements).
+// ---------------------------------------------------------------------------
+struct RingPlan {
+  std::vector<std::vector<dlc_tensor>> hop_q, hop_add;  // per reduce-scatter hop
+  std::vector<dlc_tensor> gather_q, merge;
+};
+
+std::pair<int64_t, int64_t> ring_chunk(int64_t n, int32_t k, int32_t j) {
+  const int64_t m = (n + DLC_ALIGN_ELEMS - 1) / DLC_ALIGN_ELEMS;
+  const int64_t a = std::min<int64_t>(n, DLC_ALIGN_ELEMS * ((j * m) / k));
+  const int64_t b = std::min<int64_t>(n, DLC_ALIGN_ELEMS * (((j + 1) * m) / k));
+  return {a, b};
+}
+
+RingPlan ring_plan(const dlc_tensor* t, int32_t n, int32_t k, int64_t stride) {
+  RingPlan p;
+  p.hop_q.resize(k > 1 ? k - 1 : 0);
+  p.hop_add.resize(p.hop_q.size());
+  for (int32_t s = 0; s + 1 < k; ++s) {
+    for (int32_t i = 0; i < n; ++i) {
+      for (int32_t r = 0; r < k; ++r) {
+        const int32_t c = ((r - s) % k + k) % k;
+        const auto ch = ring_chunk(t[i].numel, k, c);
+        if (ch.second <= ch.first) continue;
+        const int64_t src = (int64_t)r * stride + t[i].loffset + ch.first;
+        const int64_t dst = (int64_t)((r + 1) % k) * stride + t[i].loffset + ch.first;
+        p.hop_q[s].push_back({src, src, ch.second - ch.first});
+        p.hop_add[s].push_back({dst, src, ch.second - ch.first});
+      }
+    }
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    for (int32_t r = 0; r < k; ++r) {
+      const auto ch = ring_chunk(t[i].numel, k, (r + 1) % k);
+      if (ch.second <= ch.first) continue;
+      const int64_t src = (int64_t)r * stride + t[i].loffset + ch.first;
+      p.gather_q.push_back({src, src, ch.second - ch.first});
+      p.merge.push_back({t[i].offset + ch.first, src, ch.second - ch.first});
+    }
+  }
+  return p;
+}
+
+size_t ring_workspace(const RingPlan& p) {
+  size_t most = 0;
+  auto need = [&](const std::vector<dlc_tensor>& seg) {
+    if (seg.empty()) return;
+    const Partition ps = stats_partition(seg.data(), (int32_t)seg.size());
+    const Partition pe = encode_partition(seg.data(), (int32_t)seg.size());
+    most = std::max(most, workspace_layout(ps.n_slots, pe.n_slots, (int32_t)seg.size(), 1).total);
+  };
+  for (const auto& seg : p.hop_q) need(seg);
+  need(p.gather_q);
+  return most;
 }
 
 // fragment_first: n_fragments + 1 nondecreasing offsets from 0, at least one tensor.
@@ -628,6 +688,97 @@ int32_t dlc_merge_weights(int32_t n_learners, const double* tokens, const double
   std::copy(w.begin(), w.end(), weights);
   if (merge_time) *merge_time = (int32_t)arrived.size() == n_learners && last < deadline ? last : deadline;
   return ok();
+}
+
+int32_t dlc_ring_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors, size_t* bytes) {
+  if (!bytes) return fail(DLC_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  int32_t rc = check_tensors(tensors, n_tensors, 0, false);
+  if (rc != DLC_OK) return rc;
+  // segment sizes do not depend on the row stride
+  int64_t span = 0;
+  for (int32_t i = 0; i < n_tensors; ++i) span = std::max(span, tensors[i].loffset + tensors[i].numel);
+  const int64_t stride = (span + DLC_ALIGN_ELEMS - 1) / DLC_ALIGN_ELEMS * DLC_ALIGN_ELEMS;
+  *bytes = ring_workspace(ring_plan(tensors, n_tensors, n_learners, stride));
+  return ok();
+}
+
+int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* theta_learners,
+                            int64_t learner_stride, int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                            double lr, double beta, float* accum, uint8_t* codes, float* codebook, float* range,
+                            void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  if (!theta_global || !momentum || !theta_learners || !accum || !codes || !codebook || !range)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "a buffer pointer is NULL");
+  if (!aligned256(theta_global) || !aligned256(momentum) || !aligned256(theta_learners) || !aligned256(accum) ||
+      !aligned256(codes) || !aligned256(codebook) || !aligned256(range))
+    return fail(DLC_ERR_ALIGNMENT, "device pointers must be 256-byte aligned");
+  if (!std::isfinite(lr) || !std::isfinite(beta)) return fail(DLC_ERR_INVALID_ARGUMENT, "lr and beta must be finite");
+  int32_t rc = check_tensors(tensors, n_tensors, learner_stride, true);
+  if (rc != DLC_OK) return rc;
+  const int32_t k = n_learners;
+  const int64_t flat = (int64_t)k * learner_stride;
+  const RingPlan plan = ring_plan(tensors, n_tensors, k, learner_stride);
+  if (workspace == nullptr || workspace_bytes < ring_workspace(plan))
+    return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(ring_workspace(plan)) + " bytes");
+  // every quantize call set up (and checked) before anything is enqueued
+  auto setup = [&](Common& c, const std::vector<dlc_tensor>& seg) {
+    int32_t r = setup_quant(c, nullptr, accum, flat, 1, nullptr, seg.data(), (int32_t)seg.size(), workspace,
+                            workspace_bytes, hip_stream, 0, -1, true);
+    c.args.range = reinterpret_cast<float4*>(range);
+    c.args.codes = codes;
+    c.args.codebook = codebook;
+    return r;
+  };
+  std::vector<Common> hops(plan.hop_q.size());
+  for (size_t s = 0; s < hops.size(); ++s) {
+    if (plan.hop_q[s].empty()) continue;
+    rc = setup(hops[s], plan.hop_q[s]);
+    if (rc != DLC_OK) return rc;
+  }
+  Common gather;
+  rc = setup(gather, plan.gather_q);
+  if (rc != DLC_OK) return rc;
+  dlc::MergeArgs ma;
+  const double one = 1.0;
+  rc = prepare_merge(ma, theta_global, momentum, codes, flat, 1, codebook, &one, lr, beta);
+  if (rc != DLC_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  dlc::RingArgs ra;
+  std::memset(&ra, 0, sizeof(ra));
+  ra.theta_g = theta_global;
+  ra.theta_L = theta_learners;
+  ra.stride = learner_stride;
+  ra.n_ranks = k;
+  ra.accum = accum;
+  ra.codes = codes;
+  ra.codebook = codebook;
+  // accum_r = -Delta_r
+  for (const dlc::LaunchGeom& g : broadcast_partition(tensors, n_tensors).launches) {
+    hipError_t e = dlc::launch_ring_init(ra, g, st);
+    if (e != hipSuccess) return hip_fail(e, "ring init kernel launch");
+  }
+  // reduce-scatter: quantize every rank's outgoing chunk, then the receivers add
+  for (size_t s = 0; s < hops.size(); ++s) {
+    if (plan.hop_q[s].empty()) continue;
+    rc = run_range(hops[s]);
+    if (rc == DLC_OK) rc = run_encode(hops[s]);
+    if (rc != DLC_OK) return rc;
+    ra.divisor = s + 1 == hops.size() ? (float)k : 0.0f;  // the owners' means, after the last add
+    const std::vector<dlc_tensor>& seg = plan.hop_add[s];
+    for (const dlc::LaunchGeom& g : broadcast_partition(seg.data(), (int32_t)seg.size()).launches) {
+      hipError_t e = dlc::launch_dequant_add(ra, g, st);
+      if (e != hipSuccess) return hip_fail(e, "dequantize-add kernel launch");
+    }
+  }
+  // gather: each owner's mean quantized once; every rank would receive the same
+  // message, so the merge reads it directly
+  rc = run_range(gather);
+  if (rc == DLC_OK) rc = run_encode(gather);
+  if (rc == DLC_OK) rc = run_merge(ma, plan.merge.data(), (int32_t)plan.merge.size(), 0, -1, st);
+  return rc == DLC_OK ? ok() : rc;
 }
 
 const char* dlc_last_error(void) { return g_last_error.c_str(); }

@@ -102,6 +102,20 @@ struct BroadcastArgs {
   int32_t row[kMaxLearners];      // their learner indices
 };
 
+// The ring with requantization at every hop: each rank's running sum of a chunk
+// is kept negated (accum = -sum), so that quantizing with no base (Delta =
+// fl32(0 - accum)) quantizes the sum itself.
+struct RingArgs {
+  const float* theta_g;
+  const float* theta_L;
+  int64_t stride;           // learner row length (elements); accum and codes rows likewise
+  int32_t n_ranks;
+  float* accum;             // [n_ranks][stride] negated running sums
+  const uint8_t* codes;     // [n_ranks][stride] messages
+  const float* codebook;    // [segment][256] message codebooks
+  float divisor;            // 0: none; else the sum is divided by it after the add (fp32)
+};
+
 // Kernel launchers (dlc_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
@@ -110,5 +124,10 @@ hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s)
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStream_t s);
+// tensors: (offset in theta_g, loffset in the learner rows, numel)
+hipError_t launch_ring_init(const RingArgs& a, const LaunchGeom& g, hipStream_t s);
+// segments: (destination offset in the flat accum, source offset in the flat codes, numel); the
+// codebook row of segment t is row_base + t_base + t
+hipError_t launch_dequant_add(const RingArgs& a, const LaunchGeom& g, hipStream_t s);
 
 }  // namespace dlc

@@ -155,12 +155,15 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
   const int tid = threadIdx.x;
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
-  const float* __restrict__ tg = a.theta_g + td.offset();
+  // No base (theta_g NULL): Delta = fl32(0 - theta_L); the base loads become null
+  // requests that return zeros without memory traffic.
+  const bool has_base = a.theta_g != nullptr;
+  const float* __restrict__ tg = has_base ? a.theta_g + td.offset() : learner_row(a, 0, td);
   const int kc = a.k_count;
 
   float shift[KC];  // Delta at element 0: an fp32 value, widened where used
   double s1[KC], s2[KC];
-  const float g0 = tg[0];
+  const float g0 = has_base ? tg[0] : 0.0f;
 #pragma unroll
   for (int k = 0; k < KC; ++k) {
     const float* row = learner_row(a, k < kc ? k : kc - 1, td);
@@ -173,8 +176,8 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
   if (n_full > 0) {
     const int64_t last = sp.begin + (n_full - 1) * kTile;
     auto request = [&](int item, int64_t base, float (&dst)[kVec]) {
-      const bool real = item <= kc;
-      const float* src = (item == 0 || !real) ? tg : learner_row(a, item - 1, td);
+      const bool real = item == 0 ? has_base : item <= kc;
+      const float* src = (item == 0 || item > kc) ? tg : learner_row(a, item - 1, td);
       load_tile_rsrc(tile_rsrc(src + base, real), tid, dst);
     };
     float gv[kVec], ring[kStatsRing][kVec];
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
   if (full_end < sp.end) {
     const int64_t n = sp.end - full_end;
     float gv[kVec];
-    load_tail(tg + full_end, tid, n, gv);
+    load_tail(tg + full_end, tid, has_base ? n : 0, gv);
 #pragma unroll
     for (int k = 0; k < KC; ++k) {
       if (k < kc) {
@@ -285,7 +288,7 @@ __global__ __launch_bounds__(kRangeThreads) void k_range(const QuantArgs a, cons
   S1 = r1[0];
   S2 = r2[0];
   const int li = a.learner[k];
-  const float g0 = a.theta_g[td.offset()];
+  const float g0 = a.theta_g != nullptr ? a.theta_g[td.offset()] : 0.0f;
   const float l0 = a.theta_L[(int64_t)li * a.stride + td.loffset()];
   const double shift = (double)(g0 - l0);
   const double n = (double)td.numel();
@@ -496,7 +499,8 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
   if (tid < kc) par[tid] = make_encode_par(a.range[(size_t)a.learner[a.k_base + tid] * g.n_tensors_call + rrow]);
   __syncthreads();
 
-  const float* __restrict__ tg = a.theta_g + td.offset() + sp.begin;
+  const bool has_base = a.theta_g != nullptr;  // NULL: Delta = fl32(0 - theta_L), base tiles are zeros
+  const float* __restrict__ tg = has_base ? a.theta_g + td.offset() + sp.begin : learner_row(a, 0, td) + sp.begin;
   auto codes_of = [&](int k) {
     return a.codes + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset() + sp.begin;
   };
@@ -507,7 +511,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
     // tile u of group grp of stream s (0 = theta_g, s >= 1 = learner s - 1)
     auto request = [&](float (&dst)[kVec], int64_t grp, int s, int u) {
       const int64_t tile = grp * kGroup + u;
-      const bool valid = tile < n_full;
+      const bool valid = tile < n_full && (s != 0 || has_base);
       const float* base = s == 0 ? tg : learner_row(a, s - 1, td) + sp.begin;
       load_tile_rsrc(tile_rsrc(base + (valid ? tile : 0) * kTile, valid), tid, dst);
     };
@@ -560,7 +564,7 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
   if (sp.begin + full_len < sp.end) {
     const int64_t n = sp.end - sp.begin - full_len;
     float gv[kVec];
-    load_tail(tg + full_len, tid, n, gv);
+    load_tail(tg + full_len, tid, has_base ? n : 0, gv);
     for (int k = 0; k < kc; ++k) {
       float lv[kVec];
       load_tail(learner_row(a, k, td) + sp.begin + full_len, tid, n, lv);
@@ -944,6 +948,97 @@ __global__ __launch_bounds__(kBlock) void k_broadcast(const BroadcastArgs a, con
   }
 }
 
+// ---------------------------------------------------------------------------
+// The ring with requantization at every hop (INTELLECT-1 notes, section 3.2
+// step 6 and section 4.2).
+// k_ring_init: accum_r = fl32(theta_L_r - theta_g) = -Delta_r for every rank and
+// tensor (a tile of theta_g loaded once per block tile).
+// k_dequant_add: for each message segment, the receiver's negated sum becomes
+// fl32(accum - cb[code]) = -fl32(sum + deQ(message)), then optionally
+// fl32(accum / divisor) = -fl32(mean); the segment's codebook row sits in LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kBlock) void k_ring_init(const RingArgs a, const LaunchGeom g) {
+  const int tid = threadIdx.x;
+  const Span sp = block_span(g);
+  const TensorDesc td = g.t[sp.t];
+  const float* __restrict__ tg = a.theta_g + td.offset() + sp.begin;
+  const int64_t n_full = (sp.end - sp.begin) / kTile;
+  for (int64_t tile = 0; tile < n_full; ++tile) {
+    float gv[kVec];
+    load_tile_rsrc(tile_rsrc(tg + tile * kTile, true), tid, gv);
+    for (int r = 0; r < a.n_ranks; ++r) {
+      const int64_t row = (int64_t)r * a.stride + td.loffset() + sp.begin + tile * kTile;
+      float lv[kVec];
+      load_tile_rsrc(tile_rsrc(a.theta_L + row, true), tid, lv);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) lv[e] = lv[e] - gv[e];
+      store_tile_rsrc(tile_rsrc(a.accum + row, true), tid, lv);
+    }
+  }
+  const int64_t full_len = n_full * kTile;
+  if (sp.begin + full_len < sp.end) {
+    const int64_t n = sp.end - sp.begin - full_len;
+    float gv[kVec];
+    load_tail(tg + full_len, tid, n, gv);
+    for (int r = 0; r < a.n_ranks; ++r) {
+      const int64_t row = (int64_t)r * a.stride + td.loffset() + sp.begin + full_len;
+      float lv[kVec];
+      load_tail(a.theta_L + row, tid, n, lv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (tail_valid(tid, j, c, n)) a.accum[row + elem_index(tid, j, c)] = lv[4 * j + c] - gv[4 * j + c];
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_dequant_add(const RingArgs a, const LaunchGeom g) {
+  __shared__ float cb[kBuckets];
+  const int tid = threadIdx.x;
+  const Span sp = block_span(g);
+  const TensorDesc td = g.t[sp.t];
+  cb[tid] = a.codebook[((size_t)g.row_base + g.t_base + sp.t) * kBuckets + tid];
+  __syncthreads();
+  float* __restrict__ dst = a.accum + td.offset() + sp.begin;
+  const uint8_t* __restrict__ src = a.codes + td.loffset() + sp.begin;
+  const float div = a.divisor;
+  auto update = [&](float x, uint32_t code) {
+    x = x - cb[code];
+    return div != 0.0f ? x / div : x;
+  };
+  const int64_t n_full = (sp.end - sp.begin) / kTile;
+  for (int64_t tile = 0; tile < n_full; ++tile) {
+    float xv[kVec];
+    uint32_t cw[4];
+    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(dst + tile * kTile, true);
+    load_tile_rsrc(rx, tid, xv);
+    load_codes_rsrc(src + tile * kTile, true, tid, cw);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[4 * j + c] = update(xv[4 * j + c], (cw[j] >> (8 * c)) & 0xffu);
+    }
+    store_tile_rsrc(rx, tid, xv);
+  }
+  const int64_t full_len = n_full * kTile;
+  if (sp.begin + full_len < sp.end) {
+    const int64_t n = sp.end - sp.begin - full_len;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        if (tail_valid(tid, j, c, n)) {
+          const int64_t e = full_len + elem_index(tid, j, c);
+          dst[e] = update(dst[e], src[e]);
+        }
+      }
+    }
+  }
+}
+
 template <typename K>
 hipError_t allow_lds(K kernel, size_t lds) {
   if (lds <= 65536) return hipSuccess;
@@ -1044,6 +1139,16 @@ hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStre
     case 4: hipLaunchKernelGGL(k_broadcast<16>, grid, block, 0, s, a, g); break;
     default: hipLaunchKernelGGL(k_broadcast<0>, grid, block, 0, s, a, g); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_ring_init(const RingArgs& a, const LaunchGeom& g, hipStream_t s) {
+  hipLaunchKernelGGL(k_ring_init, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_add(const RingArgs& a, const LaunchGeom& g, hipStream_t s) {
+  hipLaunchKernelGGL(k_dequant_add, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
   return hipGetLastError();
 }
 

@@ -268,6 +268,39 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
 int32_t dlc_merge_weights(int32_t n_learners, const double* tokens, const double* arrival, int32_t quorum,
                           double grace, double* weights, double* merge_time);
 
+/*
+ * dlc_ring_outer_step -- one outer step whose learners average their
+ * pseudo-gradients through a ring that requantizes at every hop (INTELLECT-1
+ * notes, section 3.2 step 6 and section 4.2: a message is quantized before it is
+ * sent; the receiver dequantizes it and adds it to its own value in fp32), as K
+ * virtual ranks on one device, all learners weighted equally.  Per tensor:
+ *   chunks   K chunks of whole 64-element groups, chunk j = [64 floor(j m / K),
+ *            64 floor((j + 1) m / K)) clipped to numel, m = ceil(numel / 64);
+ *   reduce-scatter, hops s = 0 .. K - 2: rank r quantizes its running sum of
+ *            chunk (r - s) mod K (statistics, clip, 256 buckets, codebook of
+ *            bucket means, exactly as dlc_quantize on that chunk) and rank r + 1
+ *            sets its sum to fl32(sum + deQ(message)); after the last hop each
+ *            owner divides: mean = fl32(sum / K);
+ *   gather:  each owner's mean is quantized once; every rank ends with
+ *            g = deQ(message) for every chunk, and theta_global, momentum take
+ *            the Nesterov step with that g (as dlc_merge_outer_step).
+ * The start is Delta_r = fl32(theta_global - theta_r) for every row r < K.
+ *   accum     device fp32 [n_learners][learner_stride] scratch (running sums, kept negated)
+ *   codes     device uint8 [n_learners][learner_stride]: on return, the gather messages
+ *   codebook  device fp32 [n_learners * n_tensors][256]: on return, the gather codebooks
+ *             (one row per non-empty owned chunk, tensor by tensor, rank by rank)
+ *   range     device fp32 [n_learners * n_tensors][4], likewise
+ *   workspace >= dlc_ring_workspace_bytes(n_learners, tensors, n_tensors) bytes
+ * Same layout, alignment and stream rules as the other calls; argument errors are
+ * returned before anything is enqueued.
+ */
+int32_t dlc_ring_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors, size_t* bytes);
+
+int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* theta_learners,
+                            int64_t learner_stride, int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                            double lr, double beta, float* accum, uint8_t* codes, float* codebook, float* range,
+                            void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char* dlc_last_error(void);
 
