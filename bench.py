@@ -383,12 +383,92 @@ def stale_rate(key, device, reps=5, warmup=2):
                 hbm_frac=b / (ms_ * 1e-3) / 1e9 / PEAK_HBM_GBPS)
 
 
+def ring_study(device, ks=(2, 4, 8, 14, 16), n_params=1 << 24):
+    """The ring with requantization at every hop against the star merge: relative
+    RMS error of the merged pseudo-gradient against the exact fp64 mean, for
+    growing K (4 tensors of n_params / 4, Delta ~ N(0, (1e-3)^2), theta ~ N(0,
+    0.02^2)); g is read back from the Nesterov step from zero momentum,
+    theta' = theta - lr (1 + beta) g."""
+    import torch
+    import diloco_outer_step_amd as dlc
+    lr, beta = 0.7, 0.9
+    q = n_params // 4
+    tensors = [(i * q, i * q, q) for i in range(4)]
+    g = torch.Generator(device=device)
+    g.manual_seed(123)
+    theta = torch.randn(n_params, generator=g, device=device) * 0.02
+    out = []
+    for k in ks:
+        theta_L = torch.stack([theta - torch.randn(n_params, generator=g, device=device) * 1e-3 for _ in range(k)])
+        exact = (theta.double()[None, :] - theta_L.double()).mean(0)
+        mom = torch.zeros_like(theta)
+        res = {}
+        # star: each pseudo-gradient quantized once, equal weights
+        codes, cb, rng = dlc.outputs_for(k, n_params, 4, device)
+        ws = dlc.alloc_workspace(k, tensors, device)
+        th, mo = theta.clone(), mom.clone()
+        dlc.dlc_quantize(theta, theta_L, tensors, codes, cb, rng, ws)
+        dlc.dlc_merge_outer_step(th, mo, codes, cb, [1.0] * k, tensors, lr, beta)
+        res["star"] = th
+        del codes, cb, rng, ws
+        accum, codes, cb, rng = dlc.ring_buffers(theta_L, 4)
+        ws = torch.empty(max(256, dlc.dlc_ring_workspace_bytes(k, tensors)), dtype=torch.uint8, device=device)
+        th, mo = theta.clone(), mom.clone()
+        dlc.dlc_ring_outer_step(th, mo, theta_L, tensors, accum, codes, cb, rng, ws, lr, beta)
+        res["ring"] = th
+        torch.cuda.synchronize()
+        ref = float(exact.pow(2).mean().sqrt())
+        row = {"k": k}
+        for name, th in res.items():
+            gk = (theta.double() - th.double()) / (lr * (1 + beta))
+            row[name + "_rel_rms_error"] = float((gk - exact).pow(2).mean().sqrt()) / ref
+        row["ring_over_star"] = row["ring_rel_rms_error"] / row["star_rel_rms_error"]
+        out.append(row)
+        del theta_L, accum, codes, cb, rng, ws, res
+        torch.cuda.empty_cache()
+    return out
+
+
+def ring_rate(key, device, reps=3, warmup=1):
+    """dlc_ring_outer_step over every tensor of a set, beside the star step."""
+    import statistics
+    import torch
+    import diloco_outer_step_amd as dlc
+    import workloads
+    cfg = workloads.config(key)
+    inp = workloads.fragment_inputs(cfg, list(range(len(cfg.tensors))), device)
+    k = inp.theta_L.shape[0]
+    accum, codes, cb, rng = dlc.ring_buffers(inp.theta_L, len(inp.tensors))
+    ws = torch.empty(max(256, dlc.dlc_ring_workspace_bytes(k, inp.tensors)), dtype=torch.uint8, device=device)
+    th, mo = inp.theta_g.clone(), inp.momentum.clone()
+    run = lambda: dlc.dlc_ring_outer_step(th, mo, inp.theta_L, inp.tensors, accum, codes, cb, rng, ws,
+                                          cfg.lr, cfg.beta)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms_ = statistics.median(ts)
+    n = sum(x for _, _, x in inp.tensors)
+    # init 4 + 8K; each of the K - 1 hops: stats 4, encode 5, add 9 per element of
+    # the hop; gather 9; merge 17 (one learner)
+    b = (4 + 8 * k + 18 * (k - 1) + 9 + 17) * n
+    return dict(workload=cfg.title, ms=ms_, params=n, learners=k, params_per_s=n / (ms_ * 1e-3),
+                hbm_gbps=b / (ms_ * 1e-3) / 1e9, bytes_per_param=b // n)
+
+
 def reported(device, only=None):
     """The parameter sets that are reported but not gated: the 4096^2 tensor (cold
     cache), and full 24-fragment cycles of the 135M set and of the edge mix."""
     import torch
     keys = only.split(",") if only else ["c1", "c2", "c5k1", "c5k16", "native_c2", "native_c5k1", "broadcast_c3",
-                                         "stale_c3"]
+                                         "stale_c3", "ring_study", "ring_c3"]
     out = {}
     if "c1" in keys:
         out["c1"] = single_call_cold("c1", device)
@@ -398,6 +478,16 @@ def reported(device, only=None):
         torch.cuda.empty_cache()
         print(f"# {key}: " + ", ".join(f"{n} {v['cycle_ms']:.3f} ms" for n, v in out[key].items()
                                        if isinstance(v, dict)), file=sys.stderr, flush=True)
+    if "ring_study" in keys:
+        out["ring_study"] = ring_study(device)
+        torch.cuda.empty_cache()
+        for row in out["ring_study"]:
+            print(f"# ring study K={row['k']}: star {row['star_rel_rms_error']:.3e}, ring {row['ring_rel_rms_error']:.3e}",
+                  file=sys.stderr, flush=True)
+    if "ring_c3" in keys:
+        out["ring_c3"] = ring_rate("c3", device)
+        torch.cuda.empty_cache()
+        print(f"# ring c3 {out['ring_c3']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if "stale_c3" in keys:
         out["stale_c3"] = stale_rate("c3", device)
         torch.cuda.empty_cache()
