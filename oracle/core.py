@@ -29,6 +29,9 @@ bucket index.  Sources (the pages):
         one fragment at a time and sends the updated fragment back; the
         INTELLECT-1 notes' section 3.2 step 8 likewise has every worker copy the
         updated weights before the next outer step (broadcast, outer_cycle).
+      - section "architecture", the second engineering detail, and "fault
+        tolerance" item 3: Radial-Directional Averaging averages the outer
+        gradients' directions and norms separately (rda_merge); no formula.
 
 Readings taken where the pages are silent (each also listed in the design doc):
   * sigma is the population std (ddof = 0) of the whole tensor;
@@ -41,6 +44,8 @@ Readings taken where the pages are silent (each also listed in the design doc):
     a zero total is a failed quorum and changes nothing;
   * Nesterov in the PyTorch SGD form: v <- beta v + g; theta <- theta - lr (g + beta v),
     computed in fp64 from the fp32 state and rounded back to fp32 once;
+  * Radial-Directional Averaging, per tensor on the dequantized pseudo-gradients:
+    g = (sum_i w_i ||x_i||) d / ||d|| with d = sum_i w_i x_i / ||x_i||;
   * greedy bin-packing = LPT: tensors by size descending (ties: lower index
     first), each onto the least-loaded fragment (ties: lower fragment id).
 """
@@ -208,6 +213,41 @@ def merge(codes_per_learner, codebook_per_learner, w_hat):
     return g
 
 
+def rda_merge(codes_per_learner, codebook_per_learner, w_hat):
+    """Radial-Directional Averaging (Decoupled DiLoCo digest, "architecture", the
+    second engineering detail, and "fault tolerance" item 3): instead of a plain
+    mean of the outer gradients, their directions and their norms are averaged
+    separately.  The page gives no formula; the reading taken, per tensor, on the
+    dequantized pseudo-gradients x_i in fp64, learners in index order, weight-0
+    learners skipped:
+
+        r_i = ||x_i||_2                  the learner's norm
+        u_i = x_i / r_i                  its direction (none when r_i = 0)
+        r   = sum_i w_hat_i r_i          the averaged norm
+        d   = sum_i w_hat_i u_i          the averaged direction
+        g   = r * d / ||d||_2            (g = 0 when d = 0)
+
+    so g has the averaged norm and points along the averaged direction."""
+    n = len(codes_per_learner[0])
+    r = 0.0
+    d = None
+    for codes, cb, w in zip(codes_per_learner, codebook_per_learner, w_hat):
+        if w == 0.0:
+            continue
+        x = dequantize(codes, cb).astype(np.float64)
+        r_i = float(np.sqrt(np.sum(x * x)))
+        r += w * r_i
+        if r_i > 0.0:
+            term = w * (x / r_i)
+            d = term if d is None else d + term
+    if d is None:
+        return np.zeros(n, np.float64)
+    d_norm = float(np.sqrt(np.sum(d * d)))
+    if d_norm == 0.0:
+        return np.zeros(n, np.float64)
+    return r * (d / d_norm)
+
+
 # --- stage 4: Nesterov outer step (section 3.2 step 7) ------------------------
 
 def nesterov(theta, momentum, g, lr=0.7, beta=0.9):
@@ -224,7 +264,7 @@ def nesterov(theta, momentum, g, lr=0.7, beta=0.9):
 # --- one merge call over a fragment -------------------------------------------
 
 def outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights,
-               present=None, lr=0.7, beta=0.9, given_ranges=None, bases=None):
+               present=None, lr=0.7, beta=0.9, given_ranges=None, bases=None, rule="mean"):
     """One outer step over the tensors of one fragment.
 
     theta_g, momentum : fp32 flat arrays (not modified; new copies are returned)
@@ -237,6 +277,8 @@ def outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights,
                         learner i's pseudo-gradient is taken against bases[i] (a
                         stale learner's starting point, Decoupled DiLoCo digest,
                         "fault tolerance"); the update is still applied to theta_g
+    rule              : "mean" (the weighted mean, merge) or "rda" (Radial-
+                        Directional Averaging, rda_merge)
 
     Returns dict(theta=..., momentum=..., quant={(i, t): quantize_tensor dict},
     g={t: fp64 merged pseudo-gradient}).  Raises NoQuorum when all weights are 0.
@@ -262,7 +304,7 @@ def outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights,
             codes.append(q["codes"])
             cbs.append(q["codebook"])
             ws.append(w_hat[i])
-        g = merge(codes, cbs, ws)
+        g = rda_merge(codes, cbs, ws) if rule == "rda" else merge(codes, cbs, ws)
         gs[t] = g
         th[off:off + n], mom[off:off + n] = nesterov(tg, mom[off:off + n], g, lr, beta)
     return dict(theta=th, momentum=mom, quant=quant, g=gs)

@@ -58,6 +58,30 @@ def _lpt_last_tie(numel, n_fragments):
     return frag, loads
 
 
+def _rda_parts(codes_per_learner, codebook_per_learner, w_hat):
+    xs = [(w, oracle.dequantize(c, cb).astype(np.float64))
+          for c, cb, w in zip(codes_per_learner, codebook_per_learner, w_hat) if w != 0.0]
+    return xs, [float(np.sqrt(np.sum(x * x))) for _, x in xs]
+
+
+def _rda_no_renormalize(codes_per_learner, codebook_per_learner, w_hat):
+    xs, rs = _rda_parts(codes_per_learner, codebook_per_learner, w_hat)
+    r = sum(w * ri for (w, _), ri in zip(xs, rs))
+    return r * sum(w * (x / ri) for (w, x), ri in zip(xs, rs) if ri > 0)
+
+
+def _rda_plain_mean(codes_per_learner, codebook_per_learner, w_hat):
+    xs, rs = _rda_parts(codes_per_learner, codebook_per_learner, w_hat)
+    return sum(w * x for w, x in xs)
+
+
+def _rda_unweighted_norm(codes_per_learner, codebook_per_learner, w_hat):
+    xs, rs = _rda_parts(codes_per_learner, codebook_per_learner, w_hat)
+    r = sum(rs) / len(rs)
+    d = sum(w * (x / ri) for (w, x), ri in zip(xs, rs) if ri > 0)
+    return r * d / np.sqrt(np.sum(d * d))
+
+
 MUTATIONS = {
     "clip_at_5_sigma": (lambda mp: _patch(mp, "CLIP_SIGMAS", 5.0),
                         [pins.test_worked_example_range_from_printed_sigma]),
@@ -76,6 +100,13 @@ MUTATIONS = {
                         [pins.test_encode_exact_grid_boundaries]),
     "lpt_ties_to_last_fragment": (lambda mp: _patch(mp, "fragment_plan", _lpt_last_tie),
                                   [pins.test_lpt_hand_worked]),
+    "rda_direction_not_renormalized": (lambda mp: _patch(mp, "rda_merge", _rda_no_renormalize),
+                                       [lambda: pins.test_rda_norm_is_the_weighted_mean_norm(0)]),
+    "rda_plain_mean": (lambda mp: _patch(mp, "rda_merge", _rda_plain_mean),
+                       [pins.test_rda_two_equal_weights_bisect_the_angle,
+                        lambda: pins.test_rda_orthogonal_halves_closed_form(3.0, 1.0)]),
+    "rda_unweighted_norm": (lambda mp: _patch(mp, "rda_merge", _rda_unweighted_norm),
+                            [lambda: pins.test_rda_norm_is_the_weighted_mean_norm(0)]),
 }
 
 

@@ -644,3 +644,116 @@ def test_ring_error_exceeds_the_star_and_grows_with_the_ring():
         assert e_ring > e_star
         errs[k] = e_ring / e_star
     assert errs[8] > 1.5 * errs[2]
+
+
+# ---------------------------------------------------------------------------
+# Radial-Directional Averaging (Decoupled DiLoCo digest, "architecture", second
+# engineering detail): directions and norms averaged separately.  The page gives
+# no formula; these pins fix the reading g = (sum w_i ||x_i||) d / ||d||,
+# d = sum w_i x_i / ||x_i||, through properties that hold for it and fail for
+# the plausible slips (a plain mean, an unnormalized direction, unweighted
+# norms).
+# ---------------------------------------------------------------------------
+def _rda_learners(k, n=5000, seed=0):
+    rng = np.random.default_rng(seed)
+    codes, cbs, xs = [], [], []
+    for i in range(k):
+        x = (rng.standard_normal(n) * 10.0 ** rng.uniform(-4, -2) + rng.uniform(-1e-4, 1e-4)).astype(np.float32)
+        q = oracle.quantize_tensor(x)
+        codes.append(q["codes"])
+        cbs.append(q["codebook"])
+        xs.append(oracle.dequantize(q["codes"], q["codebook"]).astype(np.float64))
+    return codes, cbs, xs
+
+
+def _halves(n, first, second):
+    """codes / codebook of a vector equal to `first` on the first half, `second` on the rest."""
+    codes = np.zeros(n, np.uint8)
+    codes[: n // 2] = 1
+    cb = np.zeros(256, np.float32)
+    cb[0], cb[1] = second, first
+    return codes, cb
+
+
+def test_rda_one_learner_is_the_dequantized_delta():
+    codes, cbs, xs = _rda_learners(1)
+    np.testing.assert_allclose(oracle.rda_merge(codes, cbs, [1.0]), xs[0], rtol=1e-14, atol=0)
+
+
+def test_rda_identical_learners():
+    codes, cbs, xs = _rda_learners(1, seed=3)
+    g = oracle.rda_merge(codes * 3, cbs * 3, oracle.normalize_weights([1.0, 5.0, 0.5]))
+    np.testing.assert_allclose(g, xs[0], rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_rda_norm_is_the_weighted_mean_norm(seed):
+    codes, cbs, xs = _rda_learners(4, seed=seed)
+    w = oracle.normalize_weights([1.0, 3.0, 0.25, 2.0])
+    g = oracle.rda_merge(codes, cbs, w)
+    want = sum(wi * np.linalg.norm(x) for wi, x in zip(w, xs))
+    assert abs(np.linalg.norm(g) - want) <= 1e-12 * want
+
+
+def test_rda_two_equal_weights_bisect_the_angle():
+    codes, cbs, xs = _rda_learners(2, seed=5)
+    n0, n1 = np.linalg.norm(xs[0]), np.linalg.norm(xs[1])
+    assert max(n0, n1) > 2 * min(n0, n1)  # norms far apart, so a plain mean would not bisect
+    g = oracle.rda_merge(codes, cbs, [0.5, 0.5])
+    cos = [float(g @ x) / (np.linalg.norm(g) * np.linalg.norm(x)) for x in xs]
+    assert abs(cos[0] - cos[1]) <= 1e-12
+    # the plain mean leans toward the longer vector (the pin tells them apart)
+    mean = 0.5 * (xs[0] + xs[1])
+    cm = [float(mean @ x) / (np.linalg.norm(mean) * np.linalg.norm(x)) for x in xs]
+    assert abs(cm[0] - cm[1]) > 1e-3
+
+
+@pytest.mark.parametrize("a,b", [(3.0, 1.0), (-2.0, 0.5), (0.25, -4.0)])
+def test_rda_orthogonal_halves_closed_form(a, b):
+    # x1 = a on the first half, x2 = b on the second: the directions are
+    # orthogonal, ||d|| = 1/sqrt(2), and g = (|a| + |b|) / (2 sqrt(2)) times the
+    # signs, where the plain mean would give a/2 and b/2.
+    n = 1000
+    c1, cb1 = _halves(n, np.float32(a), np.float32(0.0))
+    c2, cb2 = _halves(n, np.float32(0.0), np.float32(b))
+    g = oracle.rda_merge([c1, c2], [cb1, cb2], [0.5, 0.5])
+    mag = (abs(a) + abs(b)) / (2.0 * math.sqrt(2.0))
+    np.testing.assert_allclose(g[: n // 2], np.sign(a) * mag, rtol=1e-15)
+    np.testing.assert_allclose(g[n // 2:], np.sign(b) * mag, rtol=1e-15)
+
+
+def test_rda_opposite_learners_cancel():
+    codes, cbs, xs = _rda_learners(1, seed=7)
+    neg = [np.negative(cbs[0])]
+    g = oracle.rda_merge(codes * 2, cbs + neg, [0.5, 0.5])
+    assert np.all(g == 0.0)
+
+
+def test_rda_zero_learner_adds_no_direction():
+    # r = w1 r1 and d = w1 u1, so g = w1 x1: a learner that did not move dilutes
+    # the norm by its weight and nothing else.
+    codes, cbs, xs = _rda_learners(1, seed=8)
+    z = oracle.quantize_tensor(np.zeros(len(codes[0]), np.float32))
+    w = oracle.normalize_weights([3.0, 1.0])
+    g = oracle.rda_merge([codes[0], z["codes"]], [cbs[0], z["codebook"]], w)
+    np.testing.assert_allclose(g, 0.75 * xs[0], rtol=1e-14)
+
+
+def test_rda_scaling_one_learner_changes_only_the_norm():
+    codes, cbs, xs = _rda_learners(3, seed=9)
+    w = oracle.normalize_weights([1.0, 2.0, 1.5])
+    g = oracle.rda_merge(codes, cbs, w)
+    cbs4 = [cbs[0], (cbs[1] * np.float32(4.0)).astype(np.float32), cbs[2]]
+    g4 = oracle.rda_merge(codes, cbs4, w)
+    np.testing.assert_allclose(g4 / np.linalg.norm(g4), g / np.linalg.norm(g), rtol=1e-12, atol=1e-15)
+    grow = np.linalg.norm(g4) - np.linalg.norm(g)
+    assert abs(grow - w[1] * 3.0 * np.linalg.norm(xs[1])) <= 1e-12 * np.linalg.norm(g4)
+
+
+def test_rda_outer_step_with_one_learner_is_the_star_step():
+    theta, mom, tl, stride, tensors = _cycle_case(12, k=1)
+    a = oracle.outer_step(theta, mom, tl, stride, tensors, [1.0], rule="rda")
+    b = oracle.outer_step(theta, mom, tl, stride, tensors, [1.0])
+    for t in range(len(tensors)):
+        np.testing.assert_allclose(a["g"][t], b["g"][t], rtol=1e-14, atol=0)
+    np.testing.assert_allclose(a["theta"], b["theta"], rtol=2 ** -23, atol=0)
