@@ -463,12 +463,47 @@ def ring_rate(key, device, reps=3, warmup=1):
                 hbm_gbps=b / (ms_ * 1e-3) / 1e9, bytes_per_param=b // n)
 
 
+def rda_rate(key, device, reps=5, warmup=2):
+    """dlc_rda_outer_step over every tensor of a set."""
+    import statistics
+    import torch
+    import diloco_outer_step_amd as dlc
+    import workloads
+    cfg = workloads.config(key)
+    inp = workloads.fragment_inputs(cfg, list(range(len(cfg.tensors))), device)
+    k, stride = inp.theta_L.shape
+    t = len(inp.tensors)
+    codes, cb, rng = dlc.outputs_for(k, stride, t, device)
+    norms = torch.zeros((k, t), dtype=torch.float64, device=device)
+    ws = torch.empty(max(256, dlc.dlc_rda_workspace_bytes(k, inp.tensors)), dtype=torch.uint8, device=device)
+    th, mo = inp.theta_g.clone(), inp.momentum.clone()
+    run = lambda: dlc.dlc_rda_outer_step(th, mo, inp.theta_L, inp.tensors, inp.weights, codes, cb, rng, norms, ws,
+                                         cfg.lr, cfg.beta)
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms_ = statistics.median(ts)
+    n = sum(x for _, _, x in inp.tensors)
+    kp = sum(1 for w in inp.weights if w > 0)
+    b = (24 + 11 * kp) * n  # the star step's 24 + 10K plus one more read of the codes
+    return dict(workload=cfg.title, ms=ms_, params=n, learners=kp, params_per_s=n / (ms_ * 1e-3),
+                hbm_gbps=b / (ms_ * 1e-3) / 1e9, hbm_frac=b / (ms_ * 1e-3) / 8e12, bytes_per_param=24 + 11 * kp)
+
+
 def reported(device, only=None):
     """The parameter sets that are reported but not gated: the 4096^2 tensor (cold
     cache), and full 24-fragment cycles of the 135M set and of the edge mix."""
     import torch
     keys = only.split(",") if only else ["c1", "c2", "c5k1", "c5k16", "native_c2", "native_c5k1", "broadcast_c3",
-                                         "stale_c3", "ring_study", "ring_c3"]
+                                         "stale_c3", "ring_study", "ring_c3", "rda_c3"]
     out = {}
     if "c1" in keys:
         out["c1"] = single_call_cold("c1", device)
@@ -478,6 +513,10 @@ def reported(device, only=None):
         torch.cuda.empty_cache()
         print(f"# {key}: " + ", ".join(f"{n} {v['cycle_ms']:.3f} ms" for n, v in out[key].items()
                                        if isinstance(v, dict)), file=sys.stderr, flush=True)
+    if "rda_c3" in keys:
+        out["rda_c3"] = rda_rate("c3", device)
+        torch.cuda.empty_cache()
+        print(f"# rda c3 {out['rda_c3']['ms']:.3f} ms", file=sys.stderr, flush=True)
     if "ring_study" in keys:
         out["ring_study"] = ring_study(device)
         torch.cuda.empty_cache()

@@ -34,7 +34,7 @@ EXPORTED = (
     "dlc_fragment_plan", "dlc_workspace_bytes", "dlc_quantize_range", "dlc_quantize_encode",
     "dlc_quantize", "dlc_quantize_bases", "dlc_merge_outer_step", "dlc_merge_weights", "dlc_broadcast",
     "dlc_cycle_workspace_bytes", "dlc_outer_cycle", "dlc_ring_workspace_bytes", "dlc_ring_outer_step",
-    "dlc_last_error", "dlc_version",
+    "dlc_rda_workspace_bytes", "dlc_rda_outer_step", "dlc_last_error", "dlc_version",
 )
 
 
@@ -72,6 +72,9 @@ def _load() -> ctypes.CDLL:
         "dlc_ring_workspace_bytes": [i32, tp, i32, ctypes.POINTER(sz)],
         "dlc_ring_outer_step": [vp, vp, vp, i64, i32, tp, i32, ctypes.c_double, ctypes.c_double, vp, vp, vp, vp,
                                 vp, sz, vp],
+        "dlc_rda_workspace_bytes": [i32, tp, i32, ctypes.POINTER(sz)],
+        "dlc_rda_outer_step": [vp, vp, vp, i64, i32, tp, i32, vp, ctypes.c_double, ctypes.c_double, vp, vp, vp, vp,
+                               vp, sz, vp],
         "dlc_cycle_workspace_bytes": [i32, tp, vp, i32, ctypes.POINTER(sz)],
         "dlc_outer_cycle": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, ctypes.c_double, ctypes.c_double,
                             u32, vp, sz, vp, vp],
@@ -255,6 +258,28 @@ def dlc_ring_outer_step(theta_g, momentum, theta_L, tensors, accum, codes, codeb
     _check(_lib.dlc_ring_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k, arr, n,
                                     float(lr), float(beta), _ptr(accum), _ptr(codes), _ptr(codebook), _ptr(range_out),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def dlc_rda_workspace_bytes(n_learners: int, tensors) -> int:
+    arr, n = _tensors(tensors)
+    out = ctypes.c_size_t(0)
+    _check(_lib.dlc_rda_workspace_bytes(int(n_learners), arr, n, ctypes.byref(out)))
+    return out.value
+
+
+def dlc_rda_outer_step(theta_g, momentum, theta_L, tensors, weights, codes, codebook, range_out, sq_norms, workspace,
+                       lr=0.7, beta=0.9, stream=None):
+    """One outer step merged by Radial-Directional Averaging; sq_norms is a device
+    fp64 [K, n_tensors] output (squared norms of the dequantized pseudo-gradients)."""
+    k = theta_L.shape[0]
+    if sq_norms.dtype != torch.float64:
+        raise ValueError("sq_norms must be float64")
+    w = (ctypes.c_double * k)(*[float(x) for x in weights])
+    arr, n = _tensors(tensors)
+    _check(_lib.dlc_rda_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k, arr, n,
+                                   ctypes.cast(w, ctypes.c_void_p), float(lr), float(beta), _ptr(codes),
+                                   _ptr(codebook), _ptr(range_out), _ptr(sq_norms), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)))
 
 
 def dlc_broadcast(theta_g, theta_L, tensors, rows=None, stream=None):

@@ -386,6 +386,24 @@ size_t ring_workspace(const RingPlan& p) {
 }
 
 // fragment_first: n_fragments + 1 nondecreasing offsets from 0, at least one tensor.
+// Radial-Directional Averaging: the quantize workspace, then one fp64 direction
+// sum per merge block and one coefficient per (tensor, learner).
+struct RdaWorkspace {
+  size_t quant = 0, dir_part = 0, coef = 0, total = 0;
+};
+
+RdaWorkspace rda_workspace(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors) {
+  RdaWorkspace w;
+  const Partition ps = stats_partition(tensors, n_tensors);
+  const Partition pe = encode_partition(tensors, n_tensors);
+  const Partition pm = merge_partition(tensors, n_tensors);
+  w.quant = workspace_layout(ps.n_slots, pe.n_slots, n_tensors, n_learners).total;
+  w.dir_part = w.quant;
+  w.coef = w.dir_part + round256((size_t)pm.n_slots * sizeof(double));
+  w.total = w.coef + round256((size_t)n_tensors * (size_t)n_learners * sizeof(double));
+  return w;
+}
+
 int32_t check_fragments(const dlc_tensor* tensors, const int32_t* fragment_first, int32_t n_fragments) {
   if (!tensors || !fragment_first) return fail(DLC_ERR_INVALID_ARGUMENT, "tensors and fragment_first must not be NULL");
   if (n_fragments < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "n_fragments must be >= 1");
@@ -778,6 +796,67 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
   rc = run_range(gather);
   if (rc == DLC_OK) rc = run_encode(gather);
   if (rc == DLC_OK) rc = run_merge(ma, plan.merge.data(), (int32_t)plan.merge.size(), 0, -1, st);
+  return rc == DLC_OK ? ok() : rc;
+}
+
+int32_t dlc_rda_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors, size_t* bytes) {
+  if (!bytes) return fail(DLC_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  int32_t rc = check_tensors(tensors, n_tensors, 0, false);
+  if (rc != DLC_OK) return rc;
+  *bytes = rda_workspace(n_learners, tensors, n_tensors).total;
+  return ok();
+}
+
+int32_t dlc_rda_outer_step(float* theta_global, float* momentum, const float* theta_learners,
+                           int64_t learner_stride, int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                           const double* weights, double lr, double beta, uint8_t* codes, float* codebook,
+                           float* range, double* sq_norms, void* workspace, size_t workspace_bytes,
+                           void* hip_stream) {
+  dlc::MergeArgs ma;
+  int32_t rc = prepare_merge(ma, theta_global, momentum, codes, learner_stride, n_learners, codebook, weights, lr, beta);
+  if (rc != DLC_OK) return rc;
+  if (!range || !sq_norms) return fail(DLC_ERR_INVALID_ARGUMENT, "range and sq_norms must not be NULL");
+  if (!aligned256(range) || !aligned256(sq_norms))
+    return fail(DLC_ERR_ALIGNMENT, "range and sq_norms must be 256-byte aligned");
+  rc = check_tensors(tensors, n_tensors, learner_stride, true);
+  if (rc != DLC_OK) return rc;
+  const RdaWorkspace rw = rda_workspace(n_learners, tensors, n_tensors);
+  if (workspace == nullptr || workspace_bytes < rw.total)
+    return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(rw.total) + " bytes");
+  // learners with a positive weight are quantized and merged
+  std::vector<uint8_t> present(n_learners);
+  for (int32_t i = 0; i < n_learners; ++i) present[i] = weights[i] > 0.0 ? 1 : 0;
+  Common c;
+  rc = setup_quant(c, theta_global, theta_learners, learner_stride, n_learners, present.data(), tensors, n_tensors,
+                   workspace, rw.quant, hip_stream);
+  if (rc != DLC_OK) return rc;
+  c.args.range = reinterpret_cast<float4*>(range);
+  c.args.codes = codes;
+  c.args.codebook = codebook;
+  c.args.norm2 = sq_norms;
+  char* ws = static_cast<char*>(workspace);
+  ma.norm2 = sq_norms;
+  ma.dir_part = reinterpret_cast<double*>(ws + rw.dir_part);
+  ma.coef = nullptr;
+  double* coef = reinterpret_cast<double*>(ws + rw.coef);
+  const Partition pm = merge_partition(tensors, n_tensors);
+  rc = run_range(c);
+  if (rc == DLC_OK) rc = run_encode(c);
+  if (rc != DLC_OK) return rc;
+  const hipStream_t st = c.stream;
+  for (const dlc::LaunchGeom& g : pm.launches) {
+    hipError_t e = dlc::launch_rda_direction(ma, g, st);
+    if (e != hipSuccess) return hip_fail(e, "direction kernel launch");
+  }
+  ma.coef = coef;
+  for (const dlc::LaunchGeom& g : pm.launches) {
+    hipError_t e = dlc::launch_rda_coef(ma, g, st);
+    if (e != hipSuccess) return hip_fail(e, "coefficient kernel launch");
+  }
+  ma.dir_part = nullptr;
+  rc = run_merge(ma, tensors, n_tensors, 0, -1, st);
   return rc == DLC_OK ? ok() : rc;
 }
 

@@ -79,6 +79,8 @@ struct QuantArgs {
   double2* part_stats;      // [slot][n_present] {sum(d), sum(d^2)}, d = Delta - shift
   uint64_t* part_hist;      // [slot][n_present][256] packed (count, position sum)
   uint64_t* hist_sum;       // [slice entry][n_present][256][2] {position sum, count}, see hist_entry
+  double* norm2;            // optional [n_learners][n_tensors_call]: sum over the tensor of the
+                            // dequantized values squared, sum_c count_c * codebook_c^2 (fp64)
 };
 
 struct MergeArgs {
@@ -92,6 +94,10 @@ struct MergeArgs {
   double w_hat[kMaxLearners];
   double lr;
   double beta;
+  // Radial-Directional Averaging (all null for the weighted mean):
+  const double* norm2;      // [n_learners][rows] squared norms of the dequantized pseudo-gradients
+  double* dir_part;         // [slot] per-block sums of the squared averaged direction
+  double* coef;             // [row][n_present] coefficient of each learner's codebook in g
 };
 
 struct BroadcastArgs {
@@ -123,6 +129,10 @@ hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s)
 // histogram slices, then the codebook (one kernel when every tensor has one slice)
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
+// Radial-Directional Averaging: the squared norm of the averaged direction per
+// block, then each tensor's learner coefficients (which k_merge then uses)
+hipError_t launch_rda_direction(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
+hipError_t launch_rda_coef(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStream_t s);
 // tensors: (offset in theta_g, loffset in the learner rows, numel)
 hipError_t launch_ring_init(const RingArgs& a, const LaunchGeom& g, hipStream_t s);

@@ -616,14 +616,21 @@ __device__ __forceinline__ size_t hist_entry(const LaunchGeom& g, int t, int s) 
   return (size_t)((g.slot_base + g.t[t].block_first) / kHistSlice) + (size_t)(g.t_base + t) + (size_t)s;
 }
 
+__device__ __forceinline__ size_t codebook_row(const QuantArgs& a, const LaunchGeom& g, int k, int t) {
+  return (size_t)a.learner[k] * g.n_tensors_call + g.row_base + g.t_base + t;
+}
+
 // Codebook entry c of (present learner k, tensor t) from its bucket totals.
-__device__ __forceinline__ void write_codebook(const QuantArgs& a, const LaunchGeom& g, int k, int t, int c,
-                                               uint64_t Qb, uint64_t N) {
-  const size_t row = (size_t)a.learner[k] * g.n_tensors_call + g.row_base + g.t_base + t;
+// Returns bucket c's share of the squared norm of the dequantized tensor,
+// count_c * entry_c^2 in fp64 (a zero-variance tensor codes every element as 0).
+__device__ __forceinline__ double write_codebook(const QuantArgs& a, const LaunchGeom& g, int k, int t, int c,
+                                                 uint64_t Qb, uint64_t N) {
+  const size_t row = codebook_row(a, g, k, t);
   const float4 r = a.range[row];
   float out;
   if (!(r.z >= FLT_MIN)) {
     out = r.w;
+    N = c == 0 ? (uint64_t)g.t[t].numel() : 0;
   } else if (N > 0) {
     const int64_t Q = (int64_t)(Qb - N * (uint64_t)kHistBias);
     const EncodePar par = make_encode_par(r);
@@ -633,6 +640,20 @@ __device__ __forceinline__ void write_codebook(const QuantArgs& a, const LaunchG
     out = (float)((double)r.x + ((double)c + 0.5) * (double)r.z);
   }
   a.codebook[row * kBuckets + c] = out;
+  return (double)N * ((double)out * (double)out);
+}
+
+// Sum of one value from each of the first kBuckets threads, in a fixed pairwise
+// tree (the same order every run).  Every thread of the block calls it.
+__device__ __forceinline__ double bucket_tree_sum(double v, double* s) {
+  const int c = threadIdx.x;
+  if (c < kBuckets) s[c] = v;
+  __syncthreads();
+  for (int w = kBuckets / 2; w > 0; w >>= 1) {
+    if (c < w) s[c] += s[c + w];
+    __syncthreads();
+  }
+  return s[0];
 }
 
 // FINAL: every tensor of the launch has a single slice; write the codebook
@@ -673,17 +694,24 @@ __global__ __launch_bounds__(kBuckets * kCodebookGroups) void k_hist_reduce(cons
   sq[grp][c] = Q;
   sn[grp][c] = N;
   __syncthreads();
-  if (grp != 0) return;
-  for (int u = 1; u < kCodebookGroups; ++u) {
-    Q += sq[u][c];
-    N += sn[u][c];
+  double term = 0.0;
+  if (grp == 0) {
+    for (int u = 1; u < kCodebookGroups; ++u) {
+      Q += sq[u][c];
+      N += sn[u][c];
+    }
+    if (FINAL) {
+      term = write_codebook(a, g, k, t, c, Q, N);
+    } else {
+      uint64_t* e = a.hist_sum + ((hist_entry(g, t, sl) * a.n_present + k) * kBuckets + c) * 2;
+      e[0] = Q;
+      e[1] = N;
+    }
   }
-  if (FINAL) {
-    write_codebook(a, g, k, t, c, Q, N);
-  } else {
-    uint64_t* e = a.hist_sum + ((hist_entry(g, t, sl) * a.n_present + k) * kBuckets + c) * 2;
-    e[0] = Q;
-    e[1] = N;
+  if (FINAL && a.norm2 != nullptr) {
+    __shared__ double st[kBuckets];
+    const double n2 = bucket_tree_sum(term, st);
+    if (threadIdx.x == 0) a.norm2[codebook_row(a, g, k, t)] = n2;
   }
 }
 
@@ -699,7 +727,12 @@ __global__ __launch_bounds__(kBuckets) void k_codebook(const QuantArgs a, const 
     Qb += e[0];
     N += e[1];
   }
-  write_codebook(a, g, k, t, c, Qb, N);
+  const double term = write_codebook(a, g, k, t, c, Qb, N);
+  if (a.norm2 != nullptr) {
+    __shared__ double st[kBuckets];
+    const double n2 = bucket_tree_sum(term, st);
+    if (threadIdx.x == 0) a.norm2[codebook_row(a, g, k, t)] = n2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -761,11 +794,24 @@ __device__ __forceinline__ void store_tile_rsrc(__amdgpu_buffer_rsrc_t r, int ti
 // sequence of memory operations; the prologue ends with a round's worth of (null)
 // stores, so the static wait counts fit the first round as well as the others.
 // NR = 0: any number of learners, ring rounds counted at run time.
+//
+// Radial-Directional Averaging reuses this kernel twice.  DIR = true: the table
+// holds a_i * codebook_i[c] with a_i = w_hat_i / ||x_i|| (x_i the dequantized
+// pseudo-gradient, ||x_i||^2 from the codebook stage), theta and momentum are
+// neither read nor written, and each block writes the sum of the squared
+// averaged direction over its elements.  With a.coef set (DIR = false): the table
+// holds coef_i * codebook_i[c], coef_i = a_i * r / ||d|| from k_rda_coef.
 constexpr int kMergeRing = 4;
 constexpr int kMergeMaxRounds = 4;
 constexpr int kMergeBlock = kBlock * kMergeTiles;
 
-template <int NR>
+// a_i = w_hat_i / ||x_i|| (0 for a learner whose dequantized tensor is zero)
+__device__ __forceinline__ double rda_unit_weight(const MergeArgs& a, const LaunchGeom& g, size_t trow, int k) {
+  const double n2 = a.norm2[(size_t)a.learner[k] * g.n_tensors_call + trow];
+  return n2 > 0.0 ? a.w_hat[k] / __builtin_sqrt(n2) : 0.0;
+}
+
+template <int NR, bool DIR = false>
 __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))) void k_merge(
     const MergeArgs a, const LaunchGeom g) {
   extern __shared__ __align__(16) unsigned char smem[];
@@ -781,9 +827,13 @@ __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))
   for (int i = threadIdx.x; i < kp * kBuckets; i += kMergeBlock) {
     const int k = i >> 8, c = i & (kBuckets - 1);
     const float cb = a.codebook[((size_t)a.learner[k] * g.n_tensors_call + trow) * kBuckets + c];
-    tab[i] = a.w_hat[k] * (double)cb;
+    double w;
+    if (DIR) w = rda_unit_weight(a, g, trow, k);
+    else w = a.coef != nullptr ? a.coef[trow * kp + k] : a.w_hat[k];
+    tab[i] = w * (double)cb;
   }
   __syncthreads();
+  double dsum = 0.0;  // DIR: this thread's sum of squared direction values
 
   float* __restrict__ th = a.theta_g + td.offset();
   float* __restrict__ mv = a.momentum + td.offset();
@@ -804,7 +854,7 @@ __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))
     uint32_t ring[kMergeRing][4];
 #pragma unroll
     for (int i = 0; i < kMergeRing - 1; ++i) request(ring[i], 0, i);
-    if (NR > 0) {
+    if (NR > 0 && !DIR) {
       const __amdgpu_buffer_rsrc_t none = __builtin_amdgcn_make_buffer_rsrc(th, (short)0, 0, kBufferWord3);
       const float zero[kVec] = {};
       store_tile_rsrc(none, tid, zero);
@@ -815,10 +865,12 @@ __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))
       const int64_t tile = tile_of(r);
       const bool valid = tile < n_full;
       const int64_t base = sp.begin + (valid ? tile : 0) * kTile;
-      const __amdgpu_buffer_rsrc_t rt = tile_rsrc(th + base, valid), rv = tile_rsrc(mv + base, valid);
+      const __amdgpu_buffer_rsrc_t rt = tile_rsrc(th + base, valid && !DIR), rv = tile_rsrc(mv + base, valid && !DIR);
       float tv[kVec], vv[kVec];
-      load_tile_rsrc(rt, tid, tv);
-      load_tile_rsrc(rv, tid, vv);
+      if (!DIR) {
+        load_tile_rsrc(rt, tid, tv);
+        load_tile_rsrc(rv, tid, vv);
+      }
       double acc[kVec];
 #pragma unroll
       for (int e = 0; e < kVec; ++e) acc[e] = 0.0;
@@ -841,17 +893,26 @@ __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))
           }
         }
       }
-      nesterov16(tv, vv, acc, lr, beta);
-      store_tile_rsrc(rt, tid, tv);
-      store_tile_rsrc(rv, tid, vv);
+      if (DIR) {
+        if (valid) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) dsum += acc[e] * acc[e];
+        }
+      } else {
+        nesterov16(tv, vv, acc, lr, beta);
+        store_tile_rsrc(rt, tid, tv);
+        store_tile_rsrc(rv, tid, vv);
+      }
     }
   }
   const int64_t full_end = sp.begin + n_full * kTile;
   if (q == 0 && full_end < sp.end) {
     const int64_t n = sp.end - full_end;
     float tv[kVec], vv[kVec];
-    load_tail(th + full_end, tid, n, tv);
-    load_tail(mv + full_end, tid, n, vv);
+    if (!DIR) {
+      load_tail(th + full_end, tid, n, tv);
+      load_tail(mv + full_end, tid, n, vv);
+    }
     double acc[kVec];
 #pragma unroll
     for (int e = 0; e < kVec; ++e) acc[e] = 0.0;
@@ -866,19 +927,58 @@ __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))
         }
       }
     }
-    nesterov16(tv, vv, acc, lr, beta);
+    if (DIR) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+      for (int e = 0; e < kVec; ++e) dsum += acc[e] * acc[e];  // invalid elements hold 0
+    } else {
+      nesterov16(tv, vv, acc, lr, beta);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        if (tail_valid(tid, j, c, n)) {
-          const int64_t e = full_end + elem_index(tid, j, c);
-          th[e] = tv[4 * j + c];
-          mv[e] = vv[4 * j + c];
+      for (int j = 0; j < 4; ++j) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          if (tail_valid(tid, j, c, n)) {
+            const int64_t e = full_end + elem_index(tid, j, c);
+            th[e] = tv[4 * j + c];
+            mv[e] = vv[4 * j + c];
+          }
         }
       }
     }
   }
+  if (DIR) {
+    __shared__ double red[kMergeBlock / 64];
+    const double w = wave_sum(dsum);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = w;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      double total = 0.0;
+      for (int i = 0; i < kMergeBlock / 64; ++i) total += red[i];
+      a.dir_part[g.slot_base + blockIdx.x] = total;
+    }
+  }
+}
+
+// k_rda_coef: one block per tensor.  ||d||^2 = the tensor's block sums of the
+// squared averaged direction (strided per thread, then a fixed tree);
+// r = sum_i w_hat_i ||x_i|| in learner order; coef_i = a_i * r / ||d|| (all 0
+// when ||d|| = 0, so g = 0).
+__global__ __launch_bounds__(kBuckets) void k_rda_coef(const MergeArgs a, const LaunchGeom g) {
+  __shared__ double st[kBuckets];
+  __shared__ double scale;
+  const int t = blockIdx.x;
+  const int b1 = tensor_block_end(g, t);
+  double v = 0.0;
+  for (int b = g.t[t].block_first + threadIdx.x; b < b1; b += kBuckets) v += a.dir_part[g.slot_base + b];
+  const double d2 = bucket_tree_sum(v, st);
+  const size_t trow = (size_t)g.row_base + g.t_base + t;
+  const int kp = a.n_present;
+  if (threadIdx.x == 0) {
+    double r = 0.0;
+    for (int k = 0; k < kp; ++k) r += a.w_hat[k] * __builtin_sqrt(a.norm2[(size_t)a.learner[k] * g.n_tensors_call + trow]);
+    scale = d2 > 0.0 ? r / __builtin_sqrt(d2) : 0.0;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < kp; k += kBuckets) a.coef[trow * kp + k] = scale * rda_unit_weight(a, g, trow, k);
 }
 
 // ---------------------------------------------------------------------------
@@ -1127,6 +1227,30 @@ hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) 
     case 4: return launch_merge_r<4>(a, g, s);
     default: return launch_merge_r<0>(a, g, s);
   }
+}
+
+template <int NR>
+hipError_t launch_rda_direction_r(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) {
+  const size_t lds = (size_t)a.n_present * kBuckets * sizeof(double);
+  hipError_t e = allow_lds(k_merge<NR, true>, lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_merge<NR, true>), dim3(g.n_blocks), dim3(kMergeBlock), lds, s, a, g);
+  return hipGetLastError();
+}
+
+hipError_t launch_rda_direction(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) {
+  switch ((a.n_present + kMergeRing - 1) / kMergeRing) {
+    case 1: return launch_rda_direction_r<1>(a, g, s);
+    case 2: return launch_rda_direction_r<2>(a, g, s);
+    case 3: return launch_rda_direction_r<3>(a, g, s);
+    case 4: return launch_rda_direction_r<4>(a, g, s);
+    default: return launch_rda_direction_r<0>(a, g, s);
+  }
+}
+
+hipError_t launch_rda_coef(const MergeArgs& a, const LaunchGeom& g, hipStream_t s) {
+  hipLaunchKernelGGL(k_rda_coef, dim3(g.n_tensors), dim3(kBuckets), 0, s, a, g);
+  return hipGetLastError();
 }
 
 hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStream_t s) {

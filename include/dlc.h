@@ -301,6 +301,39 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
                             double lr, double beta, float* accum, uint8_t* codes, float* codebook, float* range,
                             void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * dlc_rda_outer_step -- one outer step whose merge is Radial-Directional
+ * Averaging (Decoupled DiLoCo digest, "architecture", the second engineering
+ * detail, with "fault tolerance" item 3: the outer gradients' directions and
+ * norms are averaged separately; the page gives no formula).  Per tensor, with
+ * x_i the dequantized pseudo-gradient of learner i (quantized exactly as
+ * dlc_quantize does) and w_hat_i = weights[i] / sum(weights) in fp64:
+ *   ||x_i||^2 = sum over the tensor of x_i^2      (fp64, from the bucket counts)
+ *   r = sum_i w_hat_i ||x_i||                      the averaged norm
+ *   d = sum_i w_hat_i x_i / ||x_i||                the averaged direction
+ *                                                  (a learner with x_i = 0 adds none)
+ *   g = r d / ||d||                                (g = 0 when d = 0)
+ * then v <- beta v + g; theta <- theta - lr (g + beta v) as dlc_merge_outer_step.
+ * Learners with weight 0 are absent: neither quantized nor read, and their rows
+ * of every output are left untouched.  Results agree with the fp64 definition up
+ * to the order of fp64 rounding (not bit for bit).
+ *   codes     device uint8 [n_learners][learner_stride], written (as dlc_quantize)
+ *   codebook  device fp32 [n_learners][n_tensors][256], written
+ *   range     device fp32 [n_learners][n_tensors][4], written
+ *   sq_norms  device fp64 [n_learners][n_tensors]: ||x_i||^2 per tensor, written
+ *   workspace >= dlc_rda_workspace_bytes(n_learners, tensors, n_tensors) bytes,
+ *             256-byte aligned, no initial contents required
+ * Errors: as dlc_quantize and dlc_merge_outer_step (DLC_ERR_NO_QUORUM when every
+ * weight is zero), all returned before anything is enqueued.
+ */
+int32_t dlc_rda_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors, size_t* bytes);
+
+int32_t dlc_rda_outer_step(float* theta_global, float* momentum, const float* theta_learners,
+                           int64_t learner_stride, int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                           const double* weights, double lr, double beta, uint8_t* codes, float* codebook,
+                           float* range, double* sq_norms, void* workspace, size_t workspace_bytes,
+                           void* hip_stream);
+
 /* Message of the last error on the calling thread ("" if none). */
 const char* dlc_last_error(void);
 

@@ -86,8 +86,9 @@ def ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(key(a) - key(b))
 
 
-def compare(gpu, orc, inp, pinned: bool, report: dict | None = None):
-    """Assert parity; returns a report dict (flip counts, exact fractions, ulp stats)."""
+def compare(gpu, orc, inp, pinned: bool, report: dict | None = None, state: bool = True):
+    """Assert parity; returns a report dict (flip counts, exact fractions, ulp stats).
+    state=False checks the quantization outputs only (codes, codebooks, ranges)."""
     rep = dict(elements=0, flips=0, range_ulp_max=0, cb_ulp_max=0, theta_exact=0, mom_exact=0,
                pairs=0, range_exact_pairs=0)
     codes_g = host(gpu["codes"])
@@ -132,6 +133,8 @@ def compare(gpu, orc, inp, pinned: bool, report: dict | None = None):
                 bound = codebook_bound(q["codebook"], q["wd"])
                 assert np.all(err[used] <= bound[used]), \
                     f"codebook outside its bound (learner {i}, tensor {ti}): max err {err[used].max():.3e}"
+        if not state:
+            continue
         th_o = orc["theta"][off:off + n].astype(np.float64)
         mo_o = orc["momentum"][off:off + n].astype(np.float64)
         th_gv = theta_g[off:off + n].astype(np.float64)

@@ -138,6 +138,51 @@ def merge(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), lr=0.7, be
                                   lr, beta, flags, None)
 
 
+def ring(k=2, spec=((0, 0, 4096),), stride=4096, lr=0.7, ws_bytes=16, accum=FAKE):
+    """ws_bytes=16 stops a call that passes every other check at the workspace check."""
+    arr, n = tens(spec)
+    return L.dlc_ring_outer_step(FAKE, FAKE, FAKE, stride, k, arr, n, lr, 0.9, accum, FAKE, FAKE, FAKE, FAKE,
+                                 ws_bytes, None)
+
+
+def rda(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), norms=FAKE, ws_bytes=16, theta=FAKE):
+    arr, n = tens(spec)
+    w = (ctypes.c_double * k)(*weights)
+    return L.dlc_rda_outer_step(theta, FAKE, FAKE, stride, k, arr, n, ctypes.cast(w, ctypes.c_void_p), 0.7, 0.9,
+                                FAKE, FAKE, FAKE, norms, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("call,code", [
+    (lambda: ring(k=0), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: ring(accum=None), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: ring(accum=FAKE + 4), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: ring(lr=float("nan")), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: ring(stride=100), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: ring(), dlc.DLC_ERR_WORKSPACE),
+    (lambda: rda(weights=(0.0, 0.0)), dlc.DLC_ERR_NO_QUORUM),
+    (lambda: rda(weights=(1.0, -1.0)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: rda(norms=None), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: rda(norms=FAKE + 8), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: rda(theta=FAKE + 4), dlc.DLC_ERR_ALIGNMENT),
+    (lambda: rda(spec=((0, 0, 0),)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: rda(k=65, weights=(1.0,) * 65), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: rda(), dlc.DLC_ERR_WORKSPACE),
+])
+def test_ring_and_rda_argument_errors(call, code):
+    assert call() == code
+    assert dlc.dlc_last_error() != ""
+
+
+def test_rda_and_ring_workspace_sizes():
+    t = [(0, 0, 1 << 22), (1 << 22, 1 << 22, 4096)]
+    q = dlc.dlc_workspace_bytes(4, t)
+    r = dlc.dlc_rda_workspace_bytes(4, t)
+    assert r > q and r % 256 == 0
+    assert dlc.dlc_ring_workspace_bytes(4, t) > 0
+    with pytest.raises(dlc.DlcError):
+        dlc.dlc_rda_workspace_bytes(0, t)
+
+
 @pytest.mark.parametrize("call,code", [
     (lambda: quantize(k=0), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: quantize(k=65), dlc.DLC_ERR_INVALID_ARGUMENT),
