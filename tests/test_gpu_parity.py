@@ -52,10 +52,17 @@ def case_inputs(name):
                 seg = inp.theta_L[i, lo:lo + n]
                 seg.copy_(torch.where(keep[lo:lo + n], seg, inp.theta_g[o:o + n]))
         return inp
+    if name == "max_learners_k64":
+        # the most learners a call takes: several statistics and encode launches
+        # per pass, and the merge's run-time learner loop
+        sizes = [1, 65, 4097, 12289, 64 * 500 + 3]
+        cfg = workloads.custom("k64", sizes, 64, weights="dirichlet", absent_p=0.2)
+        return workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV, fragment=1)
     raise KeyError(name)
 
 
-CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const", "sparse_k8"]
+CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const", "sparse_k8",
+         "max_learners_k64"]
 
 
 @pytest.mark.parametrize("name", CASES)

@@ -101,7 +101,7 @@ def make_inputs(seed, k, sizes, weights, unmoved=(), constant=()):
 SIZES = [1, 63, 65, 5000, 4096 * 3 + 1, 64 * 300 + 9, 100003]
 
 
-@pytest.mark.parametrize("k", [1, 3, 8, 16, 20])
+@pytest.mark.parametrize("k", [1, 3, 8, 16, 20, 64])
 def test_rda_against_oracle(k):
     rng = np.random.default_rng(k)
     w = [float(x) for x in rng.uniform(0.5, 3.0, k)]

@@ -62,7 +62,7 @@ def test_one_rank_equals_the_star_path():
     assert torch.equal(th, th2) and torch.equal(mo, mo2)
 
 
-@pytest.mark.parametrize("k", [2, 3, 5, 8])
+@pytest.mark.parametrize("k", [2, 3, 5, 8, 64])
 def test_constant_chunks_bit_exact(k):
     sizes = [64 * 7 + 5, 4096 * 2, 100, 64 * 40]
     tensors, stride = packed(sizes)
