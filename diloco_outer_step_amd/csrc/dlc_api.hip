@@ -343,6 +343,13 @@ std::pair<int64_t, int64_t> ring_chunk(int64_t n, int32_t k, int32_t j) {
   return {a, b};
 }
 
+// Hop 0 sends each rank's own chunk, still its pseudo-gradient: quantized with
+// theta_global as the base (segments: the chunk in theta_global, the rank's chunk
+// in the flat theta_L).  Every later message is a sum the sender received at the
+// previous hop: quantized from the flat accum with no base.  A receiver's chunk
+// has never been changed before its hop, so the dequantize-add reads its
+// pseudo-gradient from theta_global and theta_L.  With one rank the gather
+// quantizes the pseudo-gradient itself.
 RingPlan ring_plan(const dlc_tensor* t, int32_t n, int32_t k, int64_t stride) {
   RingPlan p;
   p.hop_q.resize(k > 1 ? k - 1 : 0);
@@ -353,10 +360,11 @@ RingPlan ring_plan(const dlc_tensor* t, int32_t n, int32_t k, int64_t stride) {
         const int32_t c = ((r - s) % k + k) % k;
         const auto ch = ring_chunk(t[i].numel, k, c);
         if (ch.second <= ch.first) continue;
+        const int64_t g = t[i].offset + ch.first;
         const int64_t src = (int64_t)r * stride + t[i].loffset + ch.first;
         const int64_t dst = (int64_t)((r + 1) % k) * stride + t[i].loffset + ch.first;
-        p.hop_q[s].push_back({src, src, ch.second - ch.first});
-        p.hop_add[s].push_back({dst, src, ch.second - ch.first});
+        p.hop_q[s].push_back({s == 0 ? g : src, src, ch.second - ch.first});
+        p.hop_add[s].push_back({g, dst, ch.second - ch.first});
       }
     }
   }
@@ -364,9 +372,10 @@ RingPlan ring_plan(const dlc_tensor* t, int32_t n, int32_t k, int64_t stride) {
     for (int32_t r = 0; r < k; ++r) {
       const auto ch = ring_chunk(t[i].numel, k, (r + 1) % k);
       if (ch.second <= ch.first) continue;
+      const int64_t g = t[i].offset + ch.first;
       const int64_t src = (int64_t)r * stride + t[i].loffset + ch.first;
-      p.gather_q.push_back({src, src, ch.second - ch.first});
-      p.merge.push_back({t[i].offset + ch.first, src, ch.second - ch.first});
+      p.gather_q.push_back({k == 1 ? g : src, src, ch.second - ch.first});
+      p.merge.push_back({g, src, ch.second - ch.first});
     }
   }
   return p;
@@ -742,9 +751,11 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
   if (workspace == nullptr || workspace_bytes < ring_workspace(plan))
     return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(ring_workspace(plan)) + " bytes");
   // every quantize call set up (and checked) before anything is enqueued
-  auto setup = [&](Common& c, const std::vector<dlc_tensor>& seg) {
-    int32_t r = setup_quant(c, nullptr, accum, flat, 1, nullptr, seg.data(), (int32_t)seg.size(), workspace,
-                            workspace_bytes, hip_stream, 0, -1, true);
+  auto setup = [&](Common& c, const std::vector<dlc_tensor>& seg, bool with_base) {
+    int32_t r = with_base ? setup_quant(c, theta_global, theta_learners, flat, 1, nullptr, seg.data(),
+                                        (int32_t)seg.size(), workspace, workspace_bytes, hip_stream)
+                          : setup_quant(c, nullptr, accum, flat, 1, nullptr, seg.data(), (int32_t)seg.size(),
+                                        workspace, workspace_bytes, hip_stream, 0, -1, true);
     c.args.range = reinterpret_cast<float4*>(range);
     c.args.codes = codes;
     c.args.codebook = codebook;
@@ -753,11 +764,11 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
   std::vector<Common> hops(plan.hop_q.size());
   for (size_t s = 0; s < hops.size(); ++s) {
     if (plan.hop_q[s].empty()) continue;
-    rc = setup(hops[s], plan.hop_q[s]);
+    rc = setup(hops[s], plan.hop_q[s], s == 0);
     if (rc != DLC_OK) return rc;
   }
   Common gather;
-  rc = setup(gather, plan.gather_q);
+  rc = setup(gather, plan.gather_q, k == 1);
   if (rc != DLC_OK) return rc;
   dlc::MergeArgs ma;
   const double one = 1.0;
@@ -773,11 +784,6 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
   ra.accum = accum;
   ra.codes = codes;
   ra.codebook = codebook;
-  // accum_r = -Delta_r
-  for (const dlc::LaunchGeom& g : broadcast_partition(tensors, n_tensors).launches) {
-    hipError_t e = dlc::launch_ring_init(ra, g, st);
-    if (e != hipSuccess) return hip_fail(e, "ring init kernel launch");
-  }
   // reduce-scatter: quantize every rank's outgoing chunk, then the receivers add
   for (size_t s = 0; s < hops.size(); ++s) {
     if (plan.hop_q[s].empty()) continue;

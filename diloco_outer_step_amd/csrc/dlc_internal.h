@@ -109,8 +109,8 @@ struct BroadcastArgs {
 };
 
 // The ring with requantization at every hop: each rank's running sum of a chunk
-// is kept negated (accum = -sum), so that quantizing with no base (Delta =
-// fl32(0 - accum)) quantizes the sum itself.
+// it received is kept negated (accum = -sum), so that quantizing with no base
+// (Delta = fl32(0 - accum)) quantizes the sum itself.
 struct RingArgs {
   const float* theta_g;
   const float* theta_L;
@@ -134,10 +134,9 @@ hipError_t launch_merge(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_rda_direction(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_rda_coef(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStream_t s);
-// tensors: (offset in theta_g, loffset in the learner rows, numel)
-hipError_t launch_ring_init(const RingArgs& a, const LaunchGeom& g, hipStream_t s);
-// segments: (destination offset in the flat accum, source offset in the flat codes, numel); the
-// codebook row of segment t is row_base + t_base + t
+// segments: (offset of the chunk in theta_g, the receiver's offset in the flat theta_L / accum,
+// numel); the sender's codes sit one rank row earlier, cyclically; the codebook row of segment t
+// is row_base + t_base + t
 hipError_t launch_dequant_add(const RingArgs& a, const LaunchGeom& g, hipStream_t s);
 
 }  // namespace dlc

@@ -1051,50 +1051,15 @@ __global__ __launch_bounds__(kBlock) void k_broadcast(const BroadcastArgs a, con
 // ---------------------------------------------------------------------------
 // The ring with requantization at every hop (INTELLECT-1 notes, section 3.2
 // step 6 and section 4.2).
-// k_ring_init: accum_r = fl32(theta_L_r - theta_g) = -Delta_r for every rank and
-// tensor (a tile of theta_g loaded once per block tile).
-// k_dequant_add: for each message segment, the receiver's negated sum becomes
-// fl32(accum - cb[code]) = -fl32(sum + deQ(message)), then optionally
-// fl32(accum / divisor) = -fl32(mean); the segment's codebook row sits in LDS.
+// k_dequant_add: for each message segment, the receiver's chunk (which it has
+// never changed before: rank r receives chunk r - 1 - s at hop s and sends it at
+// hop s + 1) becomes -fl32(Delta + deQ(message)), stored negated as
+// fl32(fl32(theta_L - theta_g) - cb[code]) (fl32(theta_L - theta_g) = -Delta
+// exactly), then optionally fl32(x / divisor) = -fl32(mean).  The segment's
+// codebook row sits in LDS.  Segment descriptors: offset = the chunk in
+// theta_g, loffset = the receiver's chunk in the flat [ranks][stride]
+// theta_L / accum; the sender's codes sit one row earlier (cyclically).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kBlock) void k_ring_init(const RingArgs a, const LaunchGeom g) {
-  const int tid = threadIdx.x;
-  const Span sp = block_span(g);
-  const TensorDesc td = g.t[sp.t];
-  const float* __restrict__ tg = a.theta_g + td.offset() + sp.begin;
-  const int64_t n_full = (sp.end - sp.begin) / kTile;
-  for (int64_t tile = 0; tile < n_full; ++tile) {
-    float gv[kVec];
-    load_tile_rsrc(tile_rsrc(tg + tile * kTile, true), tid, gv);
-    for (int r = 0; r < a.n_ranks; ++r) {
-      const int64_t row = (int64_t)r * a.stride + td.loffset() + sp.begin + tile * kTile;
-      float lv[kVec];
-      load_tile_rsrc(tile_rsrc(a.theta_L + row, true), tid, lv);
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) lv[e] = lv[e] - gv[e];
-      store_tile_rsrc(tile_rsrc(a.accum + row, true), tid, lv);
-    }
-  }
-  const int64_t full_len = n_full * kTile;
-  if (sp.begin + full_len < sp.end) {
-    const int64_t n = sp.end - sp.begin - full_len;
-    float gv[kVec];
-    load_tail(tg + full_len, tid, n, gv);
-    for (int r = 0; r < a.n_ranks; ++r) {
-      const int64_t row = (int64_t)r * a.stride + td.loffset() + sp.begin + full_len;
-      float lv[kVec];
-      load_tail(a.theta_L + row, tid, n, lv);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (tail_valid(tid, j, c, n)) a.accum[row + elem_index(tid, j, c)] = lv[4 * j + c] - gv[4 * j + c];
-        }
-      }
-    }
-  }
-}
-
 __global__ __launch_bounds__(kBlock) void k_dequant_add(const RingArgs a, const LaunchGeom g) {
   __shared__ float cb[kBuckets];
   const int tid = threadIdx.x;
@@ -1102,26 +1067,56 @@ __global__ __launch_bounds__(kBlock) void k_dequant_add(const RingArgs a, const 
   const TensorDesc td = g.t[sp.t];
   cb[tid] = a.codebook[((size_t)g.row_base + g.t_base + sp.t) * kBuckets + tid];
   __syncthreads();
-  float* __restrict__ dst = a.accum + td.offset() + sp.begin;
-  const uint8_t* __restrict__ src = a.codes + td.loffset() + sp.begin;
+  const int64_t dst0 = td.loffset();
+  const int64_t src0 = dst0 >= a.stride ? dst0 - a.stride : dst0 + (int64_t)(a.n_ranks - 1) * a.stride;
+  float* __restrict__ dst = a.accum + dst0 + sp.begin;
+  const float* __restrict__ tl = a.theta_L + dst0 + sp.begin;
+  const float* __restrict__ tg = a.theta_g + td.offset() + sp.begin;
+  const uint8_t* __restrict__ src = a.codes + src0 + sp.begin;
   const float div = a.divisor;
-  auto update = [&](float x, uint32_t code) {
-    x = x - cb[code];
+  auto update = [&](float l, float g0, uint32_t code) {
+    const float x = (l - g0) - cb[code];
     return div != 0.0f ? x / div : x;
   };
   const int64_t n_full = (sp.end - sp.begin) / kTile;
-  for (int64_t tile = 0; tile < n_full; ++tile) {
-    float xv[kVec];
-    uint32_t cw[4];
-    const __amdgpu_buffer_rsrc_t rx = tile_rsrc(dst + tile * kTile, true);
-    load_tile_rsrc(rx, tid, xv);
-    load_codes_rsrc(src + tile * kTile, true, tid, cw);
+  // Two register slots: tile t + 1 is requested before tile t is updated and
+  // stored; requests past the block's full tiles are null (zero-record
+  // descriptors), so every iteration issues the same memory operations.
+  float lv[2][kVec], gv[2][kVec];
+  uint32_t cw[2][4];
+  auto request = [&](int slot, int64_t tile) {
+    const bool valid = tile < n_full;
+    const int64_t o = (valid ? tile : 0) * kTile;
+    load_tile_rsrc(tile_rsrc(tl + o, valid), tid, lv[slot]);
+    load_tile_rsrc(tile_rsrc(tg + o, valid), tid, gv[slot]);
+    load_codes_rsrc(src + o, valid, tid, cw[slot]);
+  };
+  auto finish = [&](int slot, int64_t tile) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) xv[4 * j + c] = update(xv[4 * j + c], (cw[j] >> (8 * c)) & 0xffu);
+      for (int c = 0; c < 4; ++c) {
+        const int e = 4 * j + c;
+        lv[slot][e] = update(lv[slot][e], gv[slot][e], (cw[slot][j] >> (8 * c)) & 0xffu);
+      }
     }
-    store_tile_rsrc(rx, tid, xv);
+    store_tile_rsrc(tile_rsrc(dst + (tile < n_full ? tile : 0) * kTile, tile < n_full), tid, lv[slot]);
+  };
+  if (n_full > 0) {
+    request(0, 0);
+    // stand-ins for the stores that precede the loop head on the back edge, so
+    // both paths into the loop carry the same memory operations (exact waits)
+    const float zero[kVec] = {};
+    store_tile_rsrc(tile_rsrc(dst, false), tid, zero);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t tile = 0; tile < n_full; tile += 2) {
+      request(1, tile + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      finish(0, tile);
+      request(0, tile + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      finish(1, tile + 1);
+    }
   }
   const int64_t full_len = n_full * kTile;
   if (sp.begin + full_len < sp.end) {
@@ -1132,7 +1127,7 @@ __global__ __launch_bounds__(kBlock) void k_dequant_add(const RingArgs a, const 
       for (int c = 0; c < 4; ++c) {
         if (tail_valid(tid, j, c, n)) {
           const int64_t e = full_len + elem_index(tid, j, c);
-          dst[e] = update(dst[e], src[e]);
+          dst[e] = update(tl[e], tg[e], src[e]);
         }
       }
     }
@@ -1263,11 +1258,6 @@ hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStre
     case 4: hipLaunchKernelGGL(k_broadcast<16>, grid, block, 0, s, a, g); break;
     default: hipLaunchKernelGGL(k_broadcast<0>, grid, block, 0, s, a, g); break;
   }
-  return hipGetLastError();
-}
-
-hipError_t launch_ring_init(const RingArgs& a, const LaunchGeom& g, hipStream_t s) {
-  hipLaunchKernelGGL(k_ring_init, dim3(g.n_blocks), dim3(kBlock), 0, s, a, g);
   return hipGetLastError();
 }
 

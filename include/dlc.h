@@ -285,7 +285,9 @@ int32_t dlc_merge_weights(int32_t n_learners, const double* tokens, const double
  *            g = deQ(message) for every chunk, and theta_global, momentum take
  *            the Nesterov step with that g (as dlc_merge_outer_step).
  * The start is Delta_r = fl32(theta_global - theta_r) for every row r < K.
- *   accum     device fp32 [n_learners][learner_stride] scratch (running sums, kept negated)
+ *   accum     device fp32 [n_learners][learner_stride] scratch: each rank's received running
+ *             sums, kept negated (hop 0 quantizes the pseudo-gradients straight from
+ *             theta_learners, so chunks a rank never receives are not written)
  *   codes     device uint8 [n_learners][learner_stride]: on return, the gather messages
  *   codebook  device fp32 [n_learners * n_tensors][256]: on return, the gather codebooks
  *             (one row per non-empty owned chunk, tensor by tensor, rank by rank)
