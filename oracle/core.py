@@ -392,6 +392,19 @@ def ring_chunks(n, k):
     return [(bounds[j], bounds[j + 1]) for j in range(k)]
 
 
+def ring_sent_chunk(rank, hop, k):
+    """The chunk rank `rank` sends to rank + 1 at reduce-scatter hop `hop`: its own
+    chunk first, then each chunk it has just received.  After k - 1 hops the rank
+    holds the whole sum of chunk ring_sent_chunk(rank, k - 1, k) = rank + 1."""
+    return (rank - hop) % k
+
+
+def ring_message(x):
+    """What the receiver gets for a sent fp32 array: its quantization, dequantized."""
+    q = quantize_tensor(x)
+    return q, dequantize(q["codes"], q["codebook"])
+
+
 def ring_outer_step(theta_g, momentum, theta_L, learner_stride, tensors, lr=0.7, beta=0.9, trace=None):
     """One outer step whose K learners (every row of theta_L, equal weights)
     average their pseudo-gradients through a ring, tensor by tensor:
@@ -417,12 +430,12 @@ def ring_outer_step(theta_g, momentum, theta_L, learner_stride, tensors, lr=0.7,
         for s in range(k - 1):
             sends = []
             for r in range(k):
-                c = (r - s) % k
+                c = ring_sent_chunk(r, s, k)
                 a, b = chunks[c]
                 if b > a:
-                    q = quantize_tensor(acc[r][a:b])
+                    q, d = ring_message(acc[r][a:b])
                     messages.append((t, s, r, c, q))
-                    sends.append((r, c, dequantize(q["codes"], q["codebook"])))
+                    sends.append((r, c, d))
             for r, c, d in sends:  # every rank sends before anyone adds
                 a, b = chunks[c]
                 dst = (r + 1) % k
@@ -431,13 +444,13 @@ def ring_outer_step(theta_g, momentum, theta_L, learner_stride, tensors, lr=0.7,
                 trace.append([x.copy() for x in acc])
         g = np.zeros(n, np.float32)
         for r in range(k):
-            c = (r + 1) % k
+            c = ring_sent_chunk(r, k - 1, k)
             a, b = chunks[c]
             if b > a:
                 mean = np.divide(acc[r][a:b], np.float32(k), dtype=np.float32)
-                q = quantize_tensor(mean)
+                q, d = ring_message(mean)
                 messages.append((t, k - 1, r, c, q))
-                g[a:b] = dequantize(q["codes"], q["codebook"])
+                g[a:b] = d
         gs[t] = g
         th[off:off + n], mom[off:off + n] = nesterov(th[off:off + n], mom[off:off + n], g.astype(np.float64), lr, beta)
     return dict(theta=th, momentum=mom, g=gs, messages=messages)

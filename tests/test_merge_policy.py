@@ -13,7 +13,7 @@ import oracle
 INF = math.inf
 
 
-@pytest.mark.parametrize("tokens, arrival, quorum, grace, want_w, want_t", [
+HAND_WORKED = [
     # quorum met at the 2nd arrival (t = 2); grace 0.5 -> deadline 2.5: learners 0 and 2
     ([100, 200, 300, 0], [1.0, 3.0, 2.0, INF], 2, 0.5, [100, 0, 300, 0], 2.5),
     # everyone arrived before the deadline: merge at the last arrival
@@ -24,7 +24,16 @@ INF = math.inf
     ([1, 1, 1], [0.0, 0.5, 1.5], 1, 1.5, [1, 1, 1], 1.5),
     # NaN = not arrived
     ([5, 7], [float("nan"), 3.0], 1, 1.0, [0, 7], 4.0),
-])
+]
+
+
+def oracle_matches_hand_worked_tables():
+    for tokens, arrival, quorum, grace, want_w, want_t in HAND_WORKED:
+        w, t = oracle.merge_weights(tokens, arrival, quorum, grace)
+        assert w == [float(x) for x in want_w] and t == want_t
+
+
+@pytest.mark.parametrize("tokens, arrival, quorum, grace, want_w, want_t", HAND_WORKED)
 def test_hand_worked(tokens, arrival, quorum, grace, want_w, want_t):
     w, t = dlc.dlc_merge_weights(tokens, arrival, quorum, grace)
     assert w == [float(x) for x in want_w] and t == want_t

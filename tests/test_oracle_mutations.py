@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import oracle.core as core
+from tests import test_merge_policy as mp
 from tests import test_oracle_pins as pins
 
 
@@ -82,6 +83,50 @@ def _rda_unweighted_norm(codes_per_learner, codebook_per_learner, w_hat):
     return r * d / np.sqrt(np.sum(d * d))
 
 
+def _ring_wrong_direction(rank, hop, k):
+    return (rank + hop) % k
+
+
+def _ring_exact_messages(x):
+    q = core.quantize_tensor(x)
+    return q, np.asarray(x, np.float32)
+
+
+def _grace_exclusive(tokens, arrival, quorum, grace):
+    k = len(tokens)
+    came = [i for i in range(k) if np.isfinite(arrival[i])]
+    if len(came) < quorum:
+        raise core.NoQuorum("quorum")
+    t_q = arrival[sorted(came, key=lambda i: (arrival[i], i))[quorum - 1]]
+    w = [float(tokens[i]) if i in came and arrival[i] < t_q + grace else 0.0 for i in range(k)]
+    if sum(w) <= 0:
+        raise core.NoQuorum("tokens")
+    return w, float(t_q + grace)
+
+
+def _quorum_off_by_one(tokens, arrival, quorum, grace):
+    return _orig_merge_weights(tokens, arrival, min(quorum + 1, len(tokens)), grace)
+
+
+_orig_merge_weights = core.merge_weights
+
+
+def _broadcast_all_rows(theta_g, theta_L, tensors, rows=None):
+    return _orig_broadcast(theta_g, theta_L, tensors, None)
+
+
+_orig_broadcast = core.broadcast
+
+
+def _bases_ignored(theta_g, momentum, theta_L, learner_stride, tensors, weights, present=None, lr=0.7, beta=0.9,
+                   given_ranges=None, bases=None, rule="mean"):
+    return _orig_outer_step(theta_g, momentum, theta_L, learner_stride, tensors, weights, present, lr, beta,
+                            given_ranges, None, rule)
+
+
+_orig_outer_step = core.outer_step
+
+
 MUTATIONS = {
     "clip_at_5_sigma": (lambda mp: _patch(mp, "CLIP_SIGMAS", 5.0),
                         [pins.test_worked_example_range_from_printed_sigma]),
@@ -107,6 +152,18 @@ MUTATIONS = {
                         lambda: pins.test_rda_orthogonal_halves_closed_form(3.0, 1.0)]),
     "rda_unweighted_norm": (lambda mp: _patch(mp, "rda_merge", _rda_unweighted_norm),
                             [lambda: pins.test_rda_norm_is_the_weighted_mean_norm(0)]),
+    "ring_chunks_travel_the_wrong_way": (lambda mp: _patch(mp, "ring_sent_chunk", _ring_wrong_direction),
+                                         [lambda: pins.test_ring_on_constant_chunks_is_the_ring_order_fp32_mean(3)]),
+    "ring_without_requantization": (lambda mp: _patch(mp, "ring_message", _ring_exact_messages),
+                                    [pins.test_ring_error_exceeds_the_star_and_grows_with_the_ring]),
+    "grace_deadline_exclusive": (lambda mp: _patch(mp, "merge_weights", _grace_exclusive),
+                                 [mp.oracle_matches_hand_worked_tables]),
+    "quorum_off_by_one": (lambda mp: _patch(mp, "merge_weights", _quorum_off_by_one),
+                          [mp.oracle_matches_hand_worked_tables]),
+    "broadcast_ignores_rows": (lambda mp: _patch(mp, "broadcast", _broadcast_all_rows),
+                               [pins.test_broadcast_copies_exactly_and_only_the_tensors]),
+    "stale_bases_ignored": (lambda mp: _patch(mp, "outer_step", _bases_ignored),
+                            [pins.test_stale_learner_without_progress_only_dilutes_the_others]),
 }
 
 
