@@ -456,10 +456,11 @@ def ring_rate(key, device, reps=3, warmup=1):
         ts.append(e0.elapsed_time(e1))
     ms_ = statistics.median(ts)
     n = sum(x for _, _, x in inp.tensors)
-    # hop 0 quantizes the pseudo-gradients (stats 8, encode 9); later hops quantize
-    # received sums (stats 4, encode 5); every add reads theta_g, theta_L, a code
-    # and writes the sum (13); gather 9; merge 17 (one learner): 22K + 12 for K >= 2
-    b = (30 + 22 * (k - 2) + 9 + 17) * n if k >= 2 else 34 * n
+    # hop 0 quantizes the pseudo-gradients (stats 8, encode 9); every add reads
+    # theta_g, theta_L and a code, writes the sum and forms the next message's
+    # statistics (13); later hops and the gather only encode (5); merge 17 (one
+    # learner): 18K + 16 for K >= 2
+    b = (17 + 13 * (k - 1) + 5 * (k - 1) + 17) * n if k >= 2 else 34 * n
     return dict(workload=cfg.title, ms=ms_, params=n, learners=k, params_per_s=n / (ms_ * 1e-3),
                 hbm_gbps=b / (ms_ * 1e-3) / 1e9, bytes_per_param=b // n)
 

@@ -332,8 +332,15 @@ int32_t run_broadcast(const float* theta_global, float* theta_learners, int64_t 
 // "learner" row of ranks * stride elements).
 // ---------------------------------------------------------------------------
 struct RingPlan {
-  std::vector<std::vector<dlc_tensor>> hop_q, hop_add;  // per reduce-scatter hop
-  std::vector<dlc_tensor> gather_q, merge;
+  // stage s < k - 1: the messages of reduce-scatter hop s; stage k - 1: the
+  // gather.  Segments (chunk offset in theta_global, the sender's offset in the
+  // flat [ranks][stride] theta_learners / accum / codes, numel), by tensor, then
+  // by sender.
+  std::vector<std::vector<dlc_tensor>> stage;
+  // add_row[s][j]: the stage-s message (its codebook row) that the sender of
+  // stage s + 1's segment j received at hop s
+  std::vector<std::vector<int32_t>> add_row;
+  std::vector<dlc_tensor> merge;
 };
 
 std::pair<int64_t, int64_t> ring_chunk(int64_t n, int32_t k, int32_t j) {
@@ -343,54 +350,51 @@ std::pair<int64_t, int64_t> ring_chunk(int64_t n, int32_t k, int32_t j) {
   return {a, b};
 }
 
-// Hop 0 sends each rank's own chunk, still its pseudo-gradient: quantized with
-// theta_global as the base (segments: the chunk in theta_global, the rank's chunk
-// in the flat theta_L).  Every later message is a sum the sender received at the
-// previous hop: quantized from the flat accum with no base.  A receiver's chunk
-// has never been changed before its hop, so the dequantize-add reads its
-// pseudo-gradient from theta_global and theta_L.  With one rank the gather
-// quantizes the pseudo-gradient itself.
+// At hop s rank r sends chunk (r - s) mod k to rank r + 1: its own chunk first,
+// then each chunk it has just received; after k - 1 hops it holds the whole sum
+// of chunk r + 1, which the gather sends.  Stage 0 holds pseudo-gradients
+// (quantized with theta_global as the base); every later message is a sum the
+// previous hop's dequantize-add wrote, with its statistics partials.  A rank's
+// chunk is untouched until the hop that delivers to it, so that add reads the
+// receiver's pseudo-gradient from theta_global and theta_learners.
 RingPlan ring_plan(const dlc_tensor* t, int32_t n, int32_t k, int64_t stride) {
   RingPlan p;
-  p.hop_q.resize(k > 1 ? k - 1 : 0);
-  p.hop_add.resize(p.hop_q.size());
-  for (int32_t s = 0; s + 1 < k; ++s) {
+  p.stage.resize(k);
+  std::vector<std::vector<int32_t>> index(k);  // [stage][tensor * k + chunk] -> segment
+  for (int32_t s = 0; s < k; ++s) {
+    index[s].assign((size_t)n * k, -1);
     for (int32_t i = 0; i < n; ++i) {
       for (int32_t r = 0; r < k; ++r) {
         const int32_t c = ((r - s) % k + k) % k;
         const auto ch = ring_chunk(t[i].numel, k, c);
         if (ch.second <= ch.first) continue;
-        const int64_t g = t[i].offset + ch.first;
-        const int64_t src = (int64_t)r * stride + t[i].loffset + ch.first;
-        const int64_t dst = (int64_t)((r + 1) % k) * stride + t[i].loffset + ch.first;
-        p.hop_q[s].push_back({s == 0 ? g : src, src, ch.second - ch.first});
-        p.hop_add[s].push_back({g, dst, ch.second - ch.first});
+        index[s][(size_t)i * k + c] = (int32_t)p.stage[s].size();
+        p.stage[s].push_back({t[i].offset + ch.first, (int64_t)r * stride + t[i].loffset + ch.first,
+                              ch.second - ch.first});
       }
     }
   }
-  for (int32_t i = 0; i < n; ++i) {
-    for (int32_t r = 0; r < k; ++r) {
-      const auto ch = ring_chunk(t[i].numel, k, (r + 1) % k);
-      if (ch.second <= ch.first) continue;
-      const int64_t g = t[i].offset + ch.first;
-      const int64_t src = (int64_t)r * stride + t[i].loffset + ch.first;
-      p.gather_q.push_back({k == 1 ? g : src, src, ch.second - ch.first});
-      p.merge.push_back({g, src, ch.second - ch.first});
+  p.add_row.resize(k - 1);
+  for (int32_t s = 0; s + 1 < k; ++s) {
+    for (int32_t i = 0; i < n; ++i) {
+      for (int32_t r = 0; r < k; ++r) {
+        const int32_t c = ((r - s - 1) % k + k) % k;  // what r sends at stage s + 1, received at hop s
+        if (index[s + 1][(size_t)i * k + c] < 0) continue;
+        p.add_row[s].push_back(index[s][(size_t)i * k + c]);
+      }
     }
   }
+  p.merge = p.stage[k - 1];
   return p;
 }
 
 size_t ring_workspace(const RingPlan& p) {
   size_t most = 0;
-  auto need = [&](const std::vector<dlc_tensor>& seg) {
-    if (seg.empty()) return;
+  for (const auto& seg : p.stage) {
     const Partition ps = stats_partition(seg.data(), (int32_t)seg.size());
     const Partition pe = encode_partition(seg.data(), (int32_t)seg.size());
     most = std::max(most, workspace_layout(ps.n_slots, pe.n_slots, (int32_t)seg.size(), 1).total);
-  };
-  for (const auto& seg : p.hop_q) need(seg);
-  need(p.gather_q);
+  }
   return most;
 }
 
@@ -750,26 +754,27 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
   const RingPlan plan = ring_plan(tensors, n_tensors, k, learner_stride);
   if (workspace == nullptr || workspace_bytes < ring_workspace(plan))
     return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(ring_workspace(plan)) + " bytes");
-  // every quantize call set up (and checked) before anything is enqueued
-  auto setup = [&](Common& c, const std::vector<dlc_tensor>& seg, bool with_base) {
-    int32_t r = with_base ? setup_quant(c, theta_global, theta_learners, flat, 1, nullptr, seg.data(),
-                                        (int32_t)seg.size(), workspace, workspace_bytes, hip_stream)
-                          : setup_quant(c, nullptr, accum, flat, 1, nullptr, seg.data(), (int32_t)seg.size(),
-                                        workspace, workspace_bytes, hip_stream, 0, -1, true);
-    c.args.range = reinterpret_cast<float4*>(range);
-    c.args.codes = codes;
-    c.args.codebook = codebook;
-    return r;
-  };
-  std::vector<Common> hops(plan.hop_q.size());
-  for (size_t s = 0; s < hops.size(); ++s) {
-    if (plan.hop_q[s].empty()) continue;
-    rc = setup(hops[s], plan.hop_q[s], s == 0);
+  // Every quantize call set up (and checked) before anything is enqueued.  The
+  // range side of a stage reads theta_global and theta_learners (k_range's shift is
+  // the sender's pseudo-gradient at the segment's first element, the shift the
+  // dequantize-add used); stage 0 runs its statistics pass and encodes from them
+  // too, later stages encode the negated sums in accum with no base.
+  std::vector<Common> rng_c(k), enc_c(k);
+  for (int32_t s = 0; s < k; ++s) {
+    const std::vector<dlc_tensor>& seg = plan.stage[s];
+    rc = setup_quant(rng_c[s], theta_global, theta_learners, flat, 1, nullptr, seg.data(), (int32_t)seg.size(),
+                     workspace, workspace_bytes, hip_stream);
+    if (rc == DLC_OK && s > 0)
+      rc = setup_quant(enc_c[s], nullptr, accum, flat, 1, nullptr, seg.data(), (int32_t)seg.size(), workspace,
+                       workspace_bytes, hip_stream, 0, -1, true);
     if (rc != DLC_OK) return rc;
+    if (s == 0) enc_c[s] = rng_c[s];
+    for (Common* c : {&rng_c[s], &enc_c[s]}) {
+      c->args.range = reinterpret_cast<float4*>(range);
+      c->args.codes = codes;
+      c->args.codebook = codebook;
+    }
   }
-  Common gather;
-  rc = setup(gather, plan.gather_q, k == 1);
-  if (rc != DLC_OK) return rc;
   dlc::MergeArgs ma;
   const double one = 1.0;
   rc = prepare_merge(ma, theta_global, momentum, codes, flat, 1, codebook, &one, lr, beta);
@@ -784,24 +789,31 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
   ra.accum = accum;
   ra.codes = codes;
   ra.codebook = codebook;
-  // reduce-scatter: quantize every rank's outgoing chunk, then the receivers add
-  for (size_t s = 0; s < hops.size(); ++s) {
-    if (plan.hop_q[s].empty()) continue;
-    rc = run_range(hops[s]);
-    if (rc == DLC_OK) rc = run_encode(hops[s]);
+  for (int32_t s = 0; s < k; ++s) {
+    // this stage's messages: range (stage 0 with its statistics pass), encode, codebook
+    if (s == 0) {
+      rc = run_range(rng_c[s]);
+    } else {
+      for (const dlc::LaunchGeom& g : rng_c[s].part_stats.launches) {
+        hipError_t e = dlc::launch_range(rng_c[s].args, g, st);
+        if (e != hipSuccess) return hip_fail(e, "range kernel launch");
+      }
+    }
+    if (rc == DLC_OK) rc = run_encode(enc_c[s]);
     if (rc != DLC_OK) return rc;
-    ra.divisor = s + 1 == hops.size() ? (float)k : 0.0f;  // the owners' means, after the last add
-    const std::vector<dlc_tensor>& seg = plan.hop_add[s];
-    for (const dlc::LaunchGeom& g : broadcast_partition(seg.data(), (int32_t)seg.size()).launches) {
+    if (s + 1 == k) break;
+    // hop s: the receivers add, in the statistics partition of stage s + 1, whose
+    // partials they write; the last hop leaves the owners' means
+    ra.divisor = s + 2 == k ? (float)k : 0.0f;
+    ra.part_stats = rng_c[s + 1].args.part_stats;
+    for (const dlc::LaunchGeom& g : rng_c[s + 1].part_stats.launches) {
+      for (int32_t j = 0; j < g.n_tensors; ++j) ra.cb_row[j] = plan.add_row[s][g.t_base + j];
       hipError_t e = dlc::launch_dequant_add(ra, g, st);
       if (e != hipSuccess) return hip_fail(e, "dequantize-add kernel launch");
     }
   }
-  // gather: each owner's mean quantized once; every rank would receive the same
-  // message, so the merge reads it directly
-  rc = run_range(gather);
-  if (rc == DLC_OK) rc = run_encode(gather);
-  if (rc == DLC_OK) rc = run_merge(ma, plan.merge.data(), (int32_t)plan.merge.size(), 0, -1, st);
+  // the gather's messages reach every rank unchanged, so the merge reads them directly
+  rc = run_merge(ma, plan.merge.data(), (int32_t)plan.merge.size(), 0, -1, st);
   return rc == DLC_OK ? ok() : rc;
 }
 

@@ -120,6 +120,9 @@ struct RingArgs {
   const uint8_t* codes;     // [n_ranks][stride] messages
   const float* codebook;    // [segment][256] message codebooks
   float divisor;            // 0: none; else the sum is divided by it after the add (fp32)
+  double2* part_stats;      // [slot] {sum(d), sum(d^2)} of the new sums, d = sum - shift: the next
+                            // message's statistics partials, in the statistics partition of the segments
+  int32_t cb_row[kMaxTensorsPerLaunch];  // codebook row of the message each segment of the launch receives
 };
 
 // Kernel launchers (dlc_kernels.hip).  Each returns hipSuccess or the launch error.
@@ -135,8 +138,8 @@ hipError_t launch_rda_direction(const MergeArgs& a, const LaunchGeom& g, hipStre
 hipError_t launch_rda_coef(const MergeArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_broadcast(const BroadcastArgs& a, const LaunchGeom& g, hipStream_t s);
 // segments: (offset of the chunk in theta_g, the receiver's offset in the flat theta_L / accum,
-// numel); the sender's codes sit one rank row earlier, cyclically; the codebook row of segment t
-// is row_base + t_base + t
+// numel); the sender's codes sit one rank row earlier, cyclically; the launch geometry must be the
+// statistics partition of these segments (the partials land in its slots)
 hipError_t launch_dequant_add(const RingArgs& a, const LaunchGeom& g, hipStream_t s);
 
 }  // namespace dlc

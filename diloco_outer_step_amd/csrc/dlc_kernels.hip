@@ -1059,14 +1059,25 @@ __global__ __launch_bounds__(kBlock) void k_broadcast(const BroadcastArgs a, con
 // codebook row sits in LDS.  Segment descriptors: offset = the chunk in
 // theta_g, loffset = the receiver's chunk in the flat [ranks][stride]
 // theta_L / accum; the sender's codes sit one row earlier (cyclically).
+// The new sum is the receiver's next message, so the kernel also forms that
+// message's statistics partials exactly as k_stats would (the same partition,
+// element order, shift and reductions): d = fl32(0 - x) - shift with shift =
+// the receiver's pseudo-gradient at the segment's first element.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kBlock) void k_dequant_add(const RingArgs a, const LaunchGeom g) {
   __shared__ float cb[kBuckets];
   const int tid = threadIdx.x;
   const Span sp = block_span(g);
   const TensorDesc td = g.t[sp.t];
-  cb[tid] = a.codebook[((size_t)g.row_base + g.t_base + sp.t) * kBuckets + tid];
+  cb[tid] = a.codebook[(size_t)a.cb_row[sp.t] * kBuckets + tid];
   __syncthreads();
+  const double shift = (double)(a.theta_g[td.offset()] - a.theta_L[td.loffset()]);
+  double s1 = 0.0, s2 = 0.0;
+  auto accumulate = [&](float x) {
+    const double d = (double)(0.0f - x) - shift;
+    s1 += d;
+    s2 = __fma_rn(d, d, s2);
+  };
   const int64_t dst0 = td.loffset();
   const int64_t src0 = dst0 >= a.stride ? dst0 - a.stride : dst0 + (int64_t)(a.n_ranks - 1) * a.stride;
   float* __restrict__ dst = a.accum + dst0 + sp.begin;
@@ -1100,6 +1111,10 @@ __global__ __launch_bounds__(kBlock) void k_dequant_add(const RingArgs a, const 
         lv[slot][e] = update(lv[slot][e], gv[slot][e], (cw[slot][j] >> (8 * c)) & 0xffu);
       }
     }
+    if (tile < n_full) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) accumulate(lv[slot][e]);
+    }
     store_tile_rsrc(tile_rsrc(dst + (tile < n_full ? tile : 0) * kTile, tile < n_full), tid, lv[slot]);
   };
   if (n_full > 0) {
@@ -1127,10 +1142,30 @@ __global__ __launch_bounds__(kBlock) void k_dequant_add(const RingArgs a, const 
       for (int c = 0; c < 4; ++c) {
         if (tail_valid(tid, j, c, n)) {
           const int64_t e = full_len + elem_index(tid, j, c);
-          dst[e] = update(tl[e], tg[e], src[e]);
+          const float x = update(tl[e], tg[e], src[e]);
+          dst[e] = x;
+          accumulate(x);
         }
       }
     }
+  }
+  // the block's partials, reduced as k_stats reduces them
+  __shared__ double red[2][kWaves];
+  const int lane = tid & 63, wave = tid >> 6;
+  const double r1 = wave_sum(s1), r2 = wave_sum(s2);
+  if (lane == 0) {
+    red[0][wave] = r1;
+    red[1][wave] = r2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double t1 = 0.0, t2 = 0.0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      t1 += red[0][w];
+      t2 += red[1][w];
+    }
+    a.part_stats[g.slot_base + blockIdx.x] = make_double2(t1, t2);
   }
 }
 
