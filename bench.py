@@ -249,7 +249,10 @@ def fragment_cycle(key, device, reps=5, warmup=2):
             torch.cuda.empty_cache()
     if cfg.absent_p != 0.0:
         cycle_ms = sum(per)  # fragments built one at a time: the sum of their medians
-    return dict(workload=cfg.title, fragments=len(per), cycle_ms=cycle_ms, fragment_ms=per,
+        timing = f"sum of per-fragment medians of {reps} (each fragment's replicas built in turn)"
+    else:
+        timing = f"three calls per fragment, enqueued back to back; median of {reps} cycles"
+    return dict(workload=cfg.title, fragments=len(per), cycle_ms=cycle_ms, fragment_ms=per, timing=timing,
                 params=total_params, params_per_s=total_params / (cycle_ms * 1e-3),
                 hbm_gbps=total_bytes / (cycle_ms * 1e-3) / 1e9,
                 hbm_frac=total_bytes / (cycle_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS)
