@@ -80,7 +80,7 @@ L = dlc._lib
 
 
 def tens(spec):
-    arr = (dlc._Tensor * len(spec))()
+    arr = (dlc._Tensor * max(1, len(spec)))()
     for i, (o, lo, n) in enumerate(spec):
         arr[i].offset, arr[i].loffset, arr[i].numel = o, lo, n
     return arr, len(spec)
@@ -171,6 +171,18 @@ def rda(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), norms=FAKE, 
 def test_ring_and_rda_argument_errors(call, code):
     assert call() == code
     assert dlc.dlc_last_error() != ""
+
+
+@pytest.mark.parametrize("call", [
+    lambda: quantize(spec=()),
+    lambda: merge(spec=()),
+    lambda: ring(spec=()),
+    lambda: rda(spec=()),
+    lambda: broadcast(spec=()),
+])
+def test_a_call_without_tensors_is_an_argument_error(call):
+    assert call() == dlc.DLC_ERR_INVALID_ARGUMENT
+    assert "n_tensors" in dlc.dlc_last_error()
 
 
 def test_rda_and_ring_workspace_sizes():
