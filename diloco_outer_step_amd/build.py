@@ -2,7 +2,7 @@
 
     python diloco_outer_step_amd/build.py
 
-(run as a script: importing the package needs the library this builds)
+(run as a script: importing the package needs the library that this script compiles)
 """
 from __future__ import annotations
 

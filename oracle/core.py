@@ -33,7 +33,7 @@ bucket index.  Sources (the pages):
         tolerance" item 3: Radial-Directional Averaging averages the outer
         gradients' directions and norms separately (rda_merge); no formula.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * sigma is the population std (ddof = 0) of the whole tensor;
   * lo = fl32(mu - 6 sigma), hi = fl32(mu + 6 sigma), wd = fl32(12 sigma / 256);
   * code = clip(floor(fl32(fl32(x - lo) / wd)), 0, 255), all IEEE fp32 RNE;
