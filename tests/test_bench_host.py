@@ -1,6 +1,7 @@
 """Host-side pieces of bench.py that need no GPU: the process-pool run of the
 oracle used for the CPU baseline reproduces oracle.outer_step exactly."""
 import numpy as np
+import pytest
 
 import bench
 import oracle
@@ -21,3 +22,21 @@ def test_pool_oracle_equals_outer_step():
         o, _, n = inp.tensors[t]
         np.testing.assert_array_equal(got["theta"][pos:pos + n], ref["theta"][o:o + n])
         np.testing.assert_array_equal(got["momentum"][pos:pos + n], ref["momentum"][o:o + n])
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_committed_counter_record_is_consistent():
+    # The benchmark reports counter traffic only for the kernel sources the counters
+    # were taken on (otherwise null); a record that applies must match the algorithmic
+    # 44 B x 852,559,872 per encode launch within 1%.
+    gb = bench.measured_traffic("k_encode", "c3")
+    if gb is None:
+        pytest.skip("the counter record was taken on other kernel sources: traffic is reported as null")
+    assert abs(gb - 44 * 852_559_872 / 1e9) <= 0.01 * 44 * 852_559_872 / 1e9
