@@ -58,11 +58,29 @@ def case_inputs(name):
         sizes = [1, 65, 4097, 12289, 64 * 500 + 3]
         cfg = workloads.custom("k64", sizes, 64, weights="dirichlet", absent_p=0.2)
         return workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV, fragment=1)
+    if name == "mean_dominated_k3":
+        # pseudo-gradients whose mean dwarfs their spread (|mu|/sigma ~ 1e7 to 5e7): lo and
+        # hi round to fp32 steps comparable to sigma, so the last bucket can span ~20 bucket
+        # widths (the histogram then keeps fewer fraction bits for the positions), or lo and
+        # hi round to the same value while wd stays normal
+        sizes = [64 * 1000 + 7, 4096 * 3, 777]
+        tensors, stride = [], 0
+        for n in sizes:
+            tensors.append((stride, stride, n))
+            stride += (n + 63) // 64 * 64
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(99)
+        theta = torch.full((stride,), 2.0, device=DEV)
+        mom = torch.zeros(stride, device=DEV)
+        theta_L = torch.empty((3, stride), device=DEV)
+        for i, sigma in enumerate([3e-8, 2e-8, 1e-7]):
+            theta_L[i] = theta - (1.0 + torch.randn(stride, generator=gen, device=DEV) * sigma)
+        return workloads.StepInputs(theta, mom, theta_L, tensors, [1.0, 2.0, 1.0], [1, 1, 1], [0, 1, 2], stride)
     raise KeyError(name)
 
 
 CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const", "sparse_k8",
-         "max_learners_k64"]
+         "max_learners_k64", "mean_dominated_k3"]
 
 
 @pytest.mark.parametrize("name", CASES)
