@@ -32,10 +32,16 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def kernel_source_hash():
+    """SHA-256 (first 16 hex digits) of the kernel and launch sources with their
+    comments and blank lines removed: a change to the code invalidates the counter
+    record, a change to a comment does not."""
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        with open(path, "rb") as f:
-            h.update(f.read())
+        with open(path, encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

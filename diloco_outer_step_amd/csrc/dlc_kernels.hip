@@ -9,10 +9,21 @@
 //   k_merge     dequantize K learners through fp64 LDS tables w_hat_i * codebook_i,
 //               sum, Nesterov update of theta and momentum, every byte read once
 //
+// and for the calls around that path:
+//   k_broadcast     the updated theta copied into every learner row (sending back)
+//   k_merge<NR, true>, k_rda_coef
+//                   Radial-Directional Averaging: the squared norm of the averaged
+//                   direction per block, then per-(tensor, learner) coefficients
+//   k_dequant_add   one hop of the ring that requantizes at every hop: the receiver
+//                   adds the dequantized message to its pseudo-gradient and forms the
+//                   statistics partials of its next message
+//
 // The quantizer follows the INTELLECT-1 reading notes, section 4.1 (per-tensor mu
 // and sigma, clip at 6 sigma, 256 equal buckets, codebook of bucket means); the
 // merge follows section 3.2 steps 6-7 and section 4.2 (dequantize, accumulate in
-// floating point, Nesterov with lr 0.7 / momentum 0.9).
+// floating point, Nesterov with lr 0.7 / momentum 0.9); the ring, section 3.2 step
+// 6 and section 4.2 (a quantized message before every send).  Sending back and
+// Radial-Directional Averaging follow the Decoupled DiLoCo digest, "architecture".
 //
 // Memory layout of a tile: kTile = 4096 elements of one tensor; wave w of the block
 // owns elements [1024 w, 1024 w + 1024) and each load instruction of a wave reads
@@ -22,8 +33,10 @@
 //
 // Floating point contraction is off for this file: every operation that has to
 // match the fp32/fp64 definition bit for bit is written as separate IEEE
-// operations; the only fused multiply-add is the explicit one that accumulates
-// sum(d^2).
+// operations.  The only fused multiply-adds are explicit ones whose rounding is
+// part of their argument: the sum(d^2) accumulation, the bucket index estimate
+// (checked against the exact division near bucket edges) and the fixed-point
+// histogram position.
 #include "dlc_internal.h"
 
 #include <cfloat>
