@@ -285,8 +285,9 @@ def single_call_cold(key, device, reps=20, warmup=3, scratch_bytes=512 << 20):
 
 def native_cycle(key, device, reps=5, warmup=2):
     """The whole fragment cycle through dlc_outer_cycle: quantize and merge on one
-    stream, on two overlapped streams, and on two streams with the update sent
-    back to the learners (dlc_broadcast after each merge)."""
+    stream, on two overlapped streams, on two streams with the update sent back to
+    the learners (dlc_broadcast after each merge), and with consecutive fragments
+    on alternating lanes (DLC_TWO_LANES)."""
     import statistics
     import torch
     import diloco_outer_step_amd as dlc
@@ -299,17 +300,19 @@ def native_cycle(key, device, reps=5, warmup=2):
     k, stride = inp.theta_L.shape
     weights = [list(inp.weights)] * cfg.n_fragments
     codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), device)
-    ws = torch.empty(max(256, dlc.dlc_cycle_workspace_bytes(k, grouped, first)), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(256, 2 * dlc.dlc_cycle_workspace_bytes(k, grouped, first)), dtype=torch.uint8,
+                     device=device)
     theta, mom, theta_L = inp.theta_g.clone(), inp.momentum.clone(), inp.theta_L.clone()
     qs = torch.cuda.current_stream()
     ms = torch.cuda.Stream()
     n_params = sum(n for _, _, n in grouped)
     out = {}
-    for name, merge_stream, bc in (("one_stream", qs, False), ("two_streams", ms, False),
-                                   ("two_streams_send_back", ms, True)):
+    for name, merge_stream, bc, lanes in (("one_stream", qs, False, False), ("two_streams", ms, False, False),
+                                          ("two_streams_send_back", ms, True, False),
+                                          ("two_lanes", ms, False, True)):
         def run():
             dlc.dlc_outer_cycle(theta, mom, theta_L if bc else inp.theta_L, grouped, first, weights, codes, cb, rng,
-                                ws, broadcast=bc, quantize_stream=qs, merge_stream=merge_stream)
+                                ws, broadcast=bc, quantize_stream=qs, merge_stream=merge_stream, two_lanes=lanes)
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()

@@ -25,6 +25,7 @@ DLC_ERR_WORKSPACE = -4
 DLC_ERR_HIP = -5
 DLC_RANGE_GIVEN = 1
 DLC_BROADCAST = 2
+DLC_TWO_LANES = 4
 DLC_MAX_LEARNERS = 64
 DLC_N_BUCKETS = 256
 DLC_ALIGN_ELEMS = 64
@@ -318,8 +319,11 @@ def dlc_cycle_workspace_bytes(n_learners: int, tensors, fragment_first) -> int:
 
 
 def dlc_outer_cycle(theta_g, momentum, theta_L, tensors, fragment_first, weights, codes, codebook, range_out,
-                    workspace, lr=0.7, beta=0.9, broadcast=False, quantize_stream=None, merge_stream=None):
-    """One outer step over every fragment; weights is [n_fragments][n_learners]."""
+                    workspace, lr=0.7, beta=0.9, broadcast=False, quantize_stream=None, merge_stream=None,
+                    two_lanes=False):
+    """One outer step over every fragment; weights is [n_fragments][n_learners].
+    two_lanes: fragments alternate between the two streams (workspace of twice
+    dlc_cycle_workspace_bytes)."""
     k = theta_L.shape[0]
     nf = len(fragment_first) - 1
     arr, _ = _tensors(tensors)
@@ -329,7 +333,8 @@ def dlc_outer_cycle(theta_g, momentum, theta_L, tensors, fragment_first, weights
     ms = qs if merge_stream is None else _stream(merge_stream)
     _check(_lib.dlc_outer_cycle(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k,
                                 ctypes.cast(w, ctypes.c_void_p), arr, fp, nf, _ptr(codes), _ptr(codebook),
-                                _ptr(range_out), float(lr), float(beta), DLC_BROADCAST if broadcast else 0,
+                                _ptr(range_out), float(lr), float(beta),
+                                (DLC_BROADCAST if broadcast else 0) | (DLC_TWO_LANES if two_lanes else 0),
                                 _ptr(workspace), workspace.numel(), qs, ms))
 
 

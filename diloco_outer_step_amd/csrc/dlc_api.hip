@@ -626,7 +626,7 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
                         const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
                         float* range, double lr, double beta, uint32_t flags, void* workspace,
                         size_t workspace_bytes, void* quantize_stream, void* merge_stream) {
-  if ((flags & ~DLC_BROADCAST) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
+  if ((flags & ~(DLC_BROADCAST | DLC_TWO_LANES)) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
   if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
   if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
     return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
@@ -636,21 +636,30 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
   rc = check_tensors(tensors, n_tensors, learner_stride, true);
   if (rc != DLC_OK) return rc;
   if (!weights) return fail(DLC_ERR_INVALID_ARGUMENT, "weights is NULL");
+  // Two lanes: the non-empty fragments alternate between the two streams, each lane
+  // with its own half of the workspace, and a fragment's quantize, merge and send
+  // back all run on its lane.
+  const bool lanes = (flags & DLC_TWO_LANES) != 0;
+  const size_t half = lanes ? (workspace_bytes / 2) & ~size_t(255) : workspace_bytes;
   // Every check before anything is enqueued: per-fragment merge arguments and quorum,
   // quantize setup (workspace size) for every non-empty fragment.
   std::vector<dlc::MergeArgs> margs(n_fragments);
   std::vector<Common> qc(n_fragments);
+  std::vector<int32_t> lane(n_fragments, 0);
   std::vector<uint8_t> present(n_learners);
+  int32_t busy = 0;
   for (int32_t f = 0; f < n_fragments; ++f) {
     const int32_t n = fragment_first[f + 1] - fragment_first[f];
     if (n == 0) continue;
+    lane[f] = lanes ? busy++ % 2 : 0;
     const double* w = weights + (size_t)f * n_learners;
     rc = prepare_merge(margs[f], theta_global, momentum, codes, learner_stride, n_learners, codebook, w, lr, beta);
     if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
     for (int32_t i = 0; i < n_learners; ++i) present[i] = w[i] > 0.0 ? 1 : 0;
+    void* lane_ws = workspace == nullptr ? nullptr : static_cast<char*>(workspace) + (size_t)lane[f] * half;
     rc = setup_quant(qc[f], theta_global, theta_learners, learner_stride, n_learners, present.data(),
-                     tensors + fragment_first[f], n, workspace, workspace_bytes, quantize_stream, fragment_first[f],
-                     n_tensors);
+                     tensors + fragment_first[f], n, lane_ws, half, lane[f] == 0 ? quantize_stream : merge_stream,
+                     fragment_first[f], n_tensors);
     if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
     qc[f].args.range = reinterpret_cast<float4*>(range);
     qc[f].args.codes = codes;
@@ -663,6 +672,15 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
     rc = run_range(qc[f]);
     if (rc == DLC_OK) rc = run_encode(qc[f]);
     if (rc != DLC_OK) return rc;
+    if (lanes) {
+      hipStream_t ls = lane[f] == 0 ? qs : ms;
+      rc = run_merge(margs[f], tensors + fragment_first[f], n, fragment_first[f], n_tensors, ls);
+      if (rc == DLC_OK && (flags & DLC_BROADCAST))
+        rc = run_broadcast(theta_global, theta_learners, learner_stride, n_learners, nullptr,
+                           tensors + fragment_first[f], n, ls);
+      if (rc != DLC_OK) return rc;
+      continue;
+    }
     // merge of this fragment after its quantization; the next fragment's
     // quantization proceeds on the quantize stream meanwhile
     hipEvent_t done;
@@ -679,12 +697,18 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
       if (rc != DLC_OK) return rc;
     }
   }
-  // the quantize stream joins the merge stream: either stream completes the cycle
+  // the streams join: either one completes the cycle
   hipEvent_t end;
   hipError_t e = hipEventCreateWithFlags(&end, hipEventDisableTiming);
   if (e == hipSuccess) e = hipEventRecord(end, ms);
   if (e == hipSuccess) e = hipStreamWaitEvent(qs, end, 0);
   if (e == hipSuccess) e = hipEventDestroy(end);
+  if (e == hipSuccess && lanes) {
+    e = hipEventCreateWithFlags(&end, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(end, qs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ms, end, 0);
+    if (e == hipSuccess) e = hipEventDestroy(end);
+  }
   if (e != hipSuccess) return hip_fail(e, "cycle event");
   return ok();
 }

@@ -66,6 +66,11 @@ extern "C" {
 /* dlc_outer_cycle flag: after each fragment's merge, copy its updated theta into
    every learner replica (dlc_broadcast). */
 #define DLC_BROADCAST 2u
+/* dlc_outer_cycle flag: the non-empty fragments alternate between the two streams
+   (lanes); each fragment's quantize, merge and send back run on its lane, with its
+   lane's half of the workspace, so consecutive fragments overlap entirely.  Needs
+   twice dlc_cycle_workspace_bytes. */
+#define DLC_TWO_LANES 4u
 
 #define DLC_MAX_LEARNERS 64
 #define DLC_N_BUCKETS 256
@@ -225,13 +230,15 @@ int32_t dlc_broadcast(const float* theta_global, float* theta_learners, int64_t 
  *   codes           device uint8 [n_learners][learner_stride]
  *   codebook        device fp32 [n_learners][n_tensors][256], row = global tensor index
  *   range           device fp32 [n_learners][n_tensors][4], row = global tensor index
- *   flags           0 or DLC_BROADCAST
- *   workspace       >= dlc_cycle_workspace_bytes(...) bytes
+ *   flags           0, DLC_BROADCAST, DLC_TWO_LANES or both
+ *   workspace       >= dlc_cycle_workspace_bytes(...) bytes (twice that with DLC_TWO_LANES)
  *   quantize_stream the quantize calls (dlc_quantize of each fragment);
  *   merge_stream    the merge (and broadcast) calls; each waits for its fragment's
  *                   quantization on the other stream through an event.  Both may
  *                   be the same stream.  At the end the quantize stream waits for
  *                   the merge stream, so synchronizing either completes the cycle.
+ *                   With DLC_TWO_LANES the two streams are instead the two lanes,
+ *                   and each waits for the other at the end.
  * Results are those of calling dlc_quantize, dlc_merge_outer_step (and
  * dlc_broadcast) fragment by fragment.  Per-call events are created and
  * destroyed inside the call.  All argument errors, including every fragment's

@@ -41,7 +41,7 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("DLC_OK", "DLC_ERR_INVALID_ARGUMENT", "DLC_ERR_ALIGNMENT", "DLC_ERR_NO_QUORUM",
                  "DLC_ERR_WORKSPACE", "DLC_ERR_HIP", "DLC_MAX_LEARNERS", "DLC_N_BUCKETS",
-                 "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS", "DLC_RANGE_GIVEN", "DLC_BROADCAST"):
+                 "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS", "DLC_RANGE_GIVEN", "DLC_BROADCAST", "DLC_TWO_LANES"):
         m = re.search(rf"#define {name} \(?(-?\d+)u?\)?", text)
         assert m and int(m.group(1)) == getattr(dlc, name), name
 
@@ -235,7 +235,8 @@ def test_rda_and_ring_workspace_sizes():
     (lambda: cycle_ws(first=(0, 1, 0)), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: cycle_ws(first=(0, 0, 0)), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: cycle_ws(first=(0,)), dlc.DLC_ERR_INVALID_ARGUMENT),
-    (lambda: cycle(flags=4), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle(flags=8), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle(flags=4, ws_bytes=64), dlc.DLC_ERR_WORKSPACE),
     (lambda: cycle(weights=((1.0, 1.0), (0.0, 0.0))), dlc.DLC_ERR_NO_QUORUM),
     (lambda: cycle(weights=((1.0, 1.0), (1.0, -2.0))), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: cycle(ws_bytes=64), dlc.DLC_ERR_WORKSPACE),

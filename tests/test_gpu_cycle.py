@@ -68,15 +68,16 @@ def cycle_inputs(seed, k, sizes, n_fragments, absent=True):
     return theta, mom, theta_L, grouped, first, weights
 
 
-def run_cycle(theta, mom, theta_L, grouped, first, weights, broadcast, two_streams):
+def run_cycle(theta, mom, theta_L, grouped, first, weights, broadcast, two_streams, two_lanes=False):
     k, stride = theta_L.shape
     theta, mom, theta_L = theta.clone(), mom.clone(), theta_L.clone()
     codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), DEV)
-    ws = torch.empty(max(256, dlc.dlc_cycle_workspace_bytes(k, grouped, first)), dtype=torch.uint8, device=DEV)
+    need = dlc.dlc_cycle_workspace_bytes(k, grouped, first) * (2 if two_lanes else 1)
+    ws = torch.empty(max(256, need), dtype=torch.uint8, device=DEV)
     qs = torch.cuda.current_stream()
     ms = torch.cuda.Stream() if two_streams else qs
     dlc.dlc_outer_cycle(theta, mom, theta_L, grouped, first, weights, codes, cb, rng, ws, broadcast=broadcast,
-                        quantize_stream=qs, merge_stream=ms)
+                        quantize_stream=qs, merge_stream=ms, two_lanes=two_lanes)
     torch.cuda.synchronize()
     return dict(theta=theta, momentum=mom, theta_L=theta_L, codes=codes, codebook=cb, range=rng)
 
@@ -118,12 +119,12 @@ def assert_same(a, b, weights, grouped, first):
                 assert torch.equal(a["range"][i, t], b["range"][i, t])
 
 
-@pytest.mark.parametrize("two_streams", [False, True])
+@pytest.mark.parametrize("two_streams,two_lanes", [(False, False), (True, False), (True, True), (False, True)])
 @pytest.mark.parametrize("broadcast", [False, True])
-def test_cycle_equals_fragment_by_fragment(two_streams, broadcast):
+def test_cycle_equals_fragment_by_fragment(two_streams, two_lanes, broadcast):
     sizes = RAGGED + [4096] * 12 + [64 * 3000 + 7] * 3 + [1 << 18]
     args = cycle_inputs(7, 5, sizes, 7)
-    a = run_cycle(*args, broadcast=broadcast, two_streams=two_streams)
+    a = run_cycle(*args, broadcast=broadcast, two_streams=two_streams, two_lanes=two_lanes)
     b = run_sequential(*args, broadcast=broadcast)
     assert_same(a, b, args[5], args[3], args[4])
 
@@ -162,3 +163,5 @@ def test_c2_cycle_with_send_back_equals_sequential():
     a = run_cycle(*args, broadcast=True, two_streams=True)
     b = run_sequential(*args, broadcast=True)
     assert_same(a, b, weights, grouped, first)
+    c = run_cycle(*args, broadcast=True, two_streams=True, two_lanes=True)
+    assert_same(c, b, weights, grouped, first)
