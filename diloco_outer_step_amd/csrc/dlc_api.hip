@@ -38,6 +38,10 @@ int32_t ok() {
 constexpr int64_t kStatsBlocks = 4096;
 constexpr int64_t kEncodeBlocks = 8192;
 constexpr int64_t kMergeTilesPerBlock = 2;
+// The direction pass of Radial-Directional Averaging reads only the codes, and
+// each block first builds its K scaled codebook tables: it does best with
+// coarser blocks than the merge.
+constexpr int64_t kDirectionBlocks = 16384;
 constexpr int64_t kBroadcastBlocks = 8192;
 // At least one full group of 4 tiles per statistics or encode block: on a
 // single 4096^2 tensor, 4-tile blocks ran the step 27% faster than 1-tile blocks
@@ -118,6 +122,10 @@ Partition encode_partition(const dlc_tensor* t, int32_t n) {
 
 Partition broadcast_partition(const dlc_tensor* t, int32_t n) {
   return make_partition(t, n, kUnlimitedTiles, kBroadcastBlocks);
+}
+
+Partition direction_partition(const dlc_tensor* t, int32_t n) {
+  return make_partition(t, n, kUnlimitedTiles, kDirectionBlocks / dlc::kMergeTiles, dlc::kMergeTiles);
 }
 
 // merge blocks work on kMergeTiles tiles side by side, kMergeTilesPerBlock in all
@@ -413,7 +421,7 @@ RdaWorkspace rda_workspace(int32_t n_learners, const dlc_tensor* tensors, int32_
   RdaWorkspace w;
   const Partition ps = stats_partition(tensors, n_tensors);
   const Partition pe = encode_partition(tensors, n_tensors);
-  const Partition pm = merge_partition(tensors, n_tensors);
+  const Partition pm = direction_partition(tensors, n_tensors);
   w.quant = workspace_layout(ps.n_slots, pe.n_slots, n_tensors, n_learners).total;
   w.dir_part = w.quant;
   w.coef = w.dir_part + round256((size_t)pm.n_slots * sizeof(double));
@@ -887,7 +895,7 @@ int32_t dlc_rda_outer_step(float* theta_global, float* momentum, const float* th
   ma.dir_part = reinterpret_cast<double*>(ws + rw.dir_part);
   ma.coef = nullptr;
   double* coef = reinterpret_cast<double*>(ws + rw.coef);
-  const Partition pm = merge_partition(tensors, n_tensors);
+  const Partition pm = direction_partition(tensors, n_tensors);
   rc = run_range(c);
   if (rc == DLC_OK) rc = run_encode(c);
   if (rc != DLC_OK) return rc;
