@@ -779,6 +779,14 @@ def main():
                      "timing": f"HIP events around the {dom} stage on the launch stream"},
         "copy_ceiling_gbps": copy["gbps"],
     }
+    # HBM bytes the counters saw per step (every kernel of the step, from the committed
+    # record of the same kernel sources) over the measured step time; null otherwise
+    counted = [measured_traffic(k, args.workload) for k in
+               ("k_stats", "k_range", "k_encode", "k_hist_reduce", "k_codebook", "k_merge")]
+    if all(c is not None for c in counted):
+        line["counter_gbps"] = sum(counted) / (res["step_ms"] * 1e-3)
+    else:
+        line["counter_gbps"] = None
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(res)
         print(f"# cpu baseline {line['cpu_baseline']['value']:.3e} params/s", file=sys.stderr, flush=True)
