@@ -247,3 +247,26 @@ def test_rda_and_ring_workspace_sizes():
 def test_argument_errors(call, code):
     assert call() == code
     assert dlc.dlc_last_error() != ""
+
+
+def test_the_package_fails_loudly_without_its_library(tmp_path):
+    """A copy of the package without libdlc.so must refuse to import (no fallback)."""
+    import shutil
+    import subprocess
+    import sys
+    src = os.path.join(ROOT, "diloco_outer_step_amd")
+    dst = tmp_path / "diloco_outer_step_amd"
+    shutil.copytree(src, dst, ignore=shutil.ignore_patterns("*.so", "__pycache__", "csrc"))
+    r = subprocess.run([sys.executable, "-c", "import diloco_outer_step_amd"], cwd=tmp_path, capture_output=True,
+                       text=True, timeout=300)
+    assert r.returncode != 0 and "libdlc.so is missing" in r.stderr
+
+
+def test_the_product_path_never_touches_the_oracle():
+    """Neither the package nor the native sources import, load or name the CPU oracle."""
+    pkg = os.path.join(ROOT, "diloco_outer_step_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert not re.search(r"\boracle\b", text), os.path.join(dirpath, f)
