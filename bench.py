@@ -395,7 +395,7 @@ def stale_rate(key, device, reps=5, warmup=2):
                 hbm_frac=b / (ms_ * 1e-3) / 1e9 / PEAK_HBM_GBPS)
 
 
-def ring_study(device, ks=(2, 4, 8, 14, 16), n_params=1 << 24):
+def ring_study(device, ks=(2, 4, 8, 14, 16, 32, 64), n_params=1 << 24):
     """The ring with requantization at every hop against the star merge: relative
     RMS error of the merged pseudo-gradient against the exact fp64 mean, for
     growing K (4 tensors of n_params / 4, Delta ~ N(0, (1e-3)^2), theta ~ N(0,
