@@ -674,6 +674,16 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
     qc[f].args.codebook = codebook;
   }
   hipStream_t qs = static_cast<hipStream_t>(quantize_stream), ms = static_cast<hipStream_t>(merge_stream);
+  if (lanes) {
+    // the second lane starts after the work already on the quantize stream (this
+    // also joins it to a capture of the quantize stream)
+    hipEvent_t fork;
+    hipError_t e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(fork, qs);
+    if (e == hipSuccess) e = hipStreamWaitEvent(ms, fork, 0);
+    if (e == hipSuccess) e = hipEventDestroy(fork);
+    if (e != hipSuccess) return hip_fail(e, "cycle event");
+  }
   for (int32_t f = 0; f < n_fragments; ++f) {
     const int32_t n = fragment_first[f + 1] - fragment_first[f];
     if (n == 0) continue;

@@ -237,8 +237,11 @@ int32_t dlc_broadcast(const float* theta_global, float* theta_learners, int64_t 
  *                   quantization on the other stream through an event.  Both may
  *                   be the same stream.  At the end the quantize stream waits for
  *                   the merge stream, so synchronizing either completes the cycle.
- *                   With DLC_TWO_LANES the two streams are instead the two lanes,
- *                   and each waits for the other at the end.
+ *                   With DLC_TWO_LANES the two streams are instead the two lanes:
+ *                   the merge stream first waits for the work already enqueued on
+ *                   the quantize stream, and each waits for the other at the end.
+ * The call can be captured in a HIP graph on the quantize stream (the merge
+ * stream joins the capture through the call's events).
  * Results are those of calling dlc_quantize, dlc_merge_outer_step (and
  * dlc_broadcast) fragment by fragment.  Per-call events are created and
  * destroyed inside the call.  All argument errors, including every fragment's

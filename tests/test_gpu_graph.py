@@ -1,0 +1,98 @@
+"""The calls of one outer step captured in a HIP graph (torch.cuda.graph) and
+replayed: nothing in them allocates, waits or clears memory through the
+runtime, so the captured launches replay bit for bit what an eager step does.
+Each replay restarts from the same state, with the program's own eager work and
+synchronizations between replays, and is checked against the eager result."""
+import pytest
+import torch
+
+import diloco_outer_step_amd as dlc
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def test_captured_step_replays_the_eager_step():
+    sizes = [1, 65, 4097, 64 * 300 + 9, 100003]
+    cfg = workloads.custom("graph", sizes, 3, weights="dirichlet")
+    inp = workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV)
+    k, stride = inp.theta_L.shape
+    # eager reference
+    codes_e, cb_e, rng_e = dlc.outputs_for(k, stride, len(sizes), DEV)
+    ws_e = dlc.alloc_workspace(k, inp.tensors, DEV)
+    th_e, mo_e = inp.theta_g.clone(), inp.momentum.clone()
+    dlc.dlc_quantize(th_e, inp.theta_L, inp.tensors, codes_e, cb_e, rng_e, ws_e)
+    dlc.dlc_merge_outer_step(th_e, mo_e, codes_e, cb_e, inp.weights, inp.tensors)
+    torch.cuda.synchronize()
+    # static buffers for the graph
+    codes, cb, rng = dlc.outputs_for(k, stride, len(sizes), DEV)
+    ws = dlc.alloc_workspace(k, inp.tensors, DEV)
+    th, mo = inp.theta_g.clone(), inp.momentum.clone()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            dlc.dlc_quantize(th, inp.theta_L, inp.tensors, codes, cb, rng, ws)
+            dlc.dlc_merge_outer_step(th, mo, codes, cb, inp.weights, inp.tensors)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        th.copy_(inp.theta_g)
+        mo.copy_(inp.momentum)
+        noise = torch.randn(1 << 20, device=DEV).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise)
+        for _, lo, n in inp.tensors:
+            assert torch.equal(codes[:, lo:lo + n], codes_e[:, lo:lo + n]), rep
+        assert torch.equal(cb, cb_e) and torch.equal(rng, rng_e), rep
+        assert torch.equal(th, th_e) and torch.equal(mo, mo_e), rep
+
+
+@pytest.mark.parametrize("two_lanes", [False, True])
+def test_captured_cycle_replays_the_eager_cycle(two_lanes):
+    """A whole fragment cycle on two streams (the second joins the capture through
+    the cycle's own events), captured once and replayed."""
+    sizes = [4096] * 6 + [64 * 1000 + 5] * 3 + [1 << 17, 777]
+    cfg = workloads.custom("graph_cycle", sizes, 4)
+    inp = workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV)
+    k, stride = inp.theta_L.shape
+    frag, _ = dlc.dlc_fragment_plan(sizes, 5)
+    grouped, first, _ = dlc.group_by_fragment(inp.tensors, frag, 5)
+    weights = [list(inp.weights)] * 5
+    need = dlc.dlc_cycle_workspace_bytes(k, grouped, first) * 2
+
+    def buffers():
+        codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), DEV)
+        ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+        return codes, cb, rng, ws, inp.theta_g.clone(), inp.momentum.clone(), inp.theta_L.clone()
+
+    codes_e, cb_e, rng_e, ws_e, th_e, mo_e, tl_e = buffers()
+    other = torch.cuda.Stream()
+    dlc.dlc_outer_cycle(th_e, mo_e, tl_e, grouped, first, weights, codes_e, cb_e, rng_e, ws_e, broadcast=True,
+                        quantize_stream=torch.cuda.current_stream(), merge_stream=other, two_lanes=two_lanes)
+    torch.cuda.synchronize()
+
+    codes, cb, rng, ws, th, mo, tl = buffers()
+    graph = torch.cuda.CUDAGraph()
+    side, other2 = torch.cuda.Stream(), torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            dlc.dlc_outer_cycle(th, mo, tl, grouped, first, weights, codes, cb, rng, ws, broadcast=True,
+                                quantize_stream=side, merge_stream=other2, two_lanes=two_lanes)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        th.copy_(inp.theta_g)
+        mo.copy_(inp.momentum)
+        tl.copy_(inp.theta_L)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(th, th_e) and torch.equal(mo, mo_e) and torch.equal(tl, tl_e), rep
+        assert torch.equal(cb, cb_e) and torch.equal(rng, rng_e), rep
