@@ -46,6 +46,7 @@ Readings taken where the pages are silent:
     computed in fp64 from the fp32 state and rounded back to fp32 once;
   * Radial-Directional Averaging, per tensor on the dequantized pseudo-gradients:
     g = (sum_i w_i ||x_i||) d / ||d|| with d = sum_i w_i x_i / ||x_i||;
+  * NaN or Inf in a pseudo-gradient is outside the contract: the oracle raises;
   * greedy bin-packing = LPT: tensors by size descending (ties: lower index
     first), each onto the least-loaded fragment (ties: lower fragment id).
 """
@@ -161,6 +162,8 @@ def quantize_tensor(x, given_range=None):
     skips the statistics and uses that range instead.
     """
     x = np.asarray(x, dtype=np.float32).ravel()
+    if not np.isfinite(x).all():
+        raise ValueError("non-finite pseudo-gradient: NaN and Inf are outside the method's contract")
     if given_range is None:
         mu, sigma = tensor_stats(x)
         lo, hi, wd, m32, degenerate = clip_range(mu, sigma)

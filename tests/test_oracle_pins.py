@@ -757,3 +757,11 @@ def test_rda_outer_step_with_one_learner_is_the_star_step():
     for t in range(len(tensors)):
         np.testing.assert_allclose(a["g"][t], b["g"][t], rtol=1e-14, atol=0)
     np.testing.assert_allclose(a["theta"], b["theta"], rtol=2 ** -23, atol=0)
+
+
+@pytest.mark.parametrize("bad", [np.nan, np.inf, -np.inf])
+def test_non_finite_pseudo_gradients_are_refused(bad):
+    x = np.zeros(100, np.float32)
+    x[37] = bad
+    with pytest.raises(ValueError):
+        oracle.quantize_tensor(x)
