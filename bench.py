@@ -287,8 +287,8 @@ def native_cycle(key, device, reps=5, warmup=2):
     """The whole fragment cycle through dlc_outer_cycle: quantize and merge on one
     stream, on two overlapped streams, on two streams with the update sent back to
     the learners (dlc_broadcast after each merge), with consecutive fragments on
-    alternating lanes (DLC_TWO_LANES), and that last cycle captured in a HIP graph
-    and replayed."""
+    alternating lanes (DLC_TWO_LANES), on three lanes (dlc_outer_cycle_lanes), and
+    the three-lane cycle captured in a HIP graph and replayed."""
     import statistics
     import torch
     import diloco_outer_step_amd as dlc
@@ -301,17 +301,22 @@ def native_cycle(key, device, reps=5, warmup=2):
     k, stride = inp.theta_L.shape
     weights = [list(inp.weights)] * cfg.n_fragments
     codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), device)
-    ws = torch.empty(max(256, 2 * dlc.dlc_cycle_workspace_bytes(k, grouped, first)), dtype=torch.uint8,
+    ws = torch.empty(max(256, 3 * dlc.dlc_cycle_workspace_bytes(k, grouped, first)), dtype=torch.uint8,
                      device=device)
     theta, mom, theta_L = inp.theta_g.clone(), inp.momentum.clone(), inp.theta_L.clone()
     qs = torch.cuda.current_stream()
     ms = torch.cuda.Stream()
     n_params = sum(n for _, _, n in grouped)
     out = {}
+    third = torch.cuda.Stream()
     for name, merge_stream, bc, lanes in (("one_stream", qs, False, False), ("two_streams", ms, False, False),
                                           ("two_streams_send_back", ms, True, False),
-                                          ("two_lanes", ms, False, True)):
+                                          ("two_lanes", ms, False, True), ("three_lanes", ms, False, 3)):
         def run():
+            if lanes == 3:
+                dlc.dlc_outer_cycle_lanes(theta, mom, inp.theta_L, grouped, first, weights, codes, cb, rng, ws,
+                                          [qs, ms, third])
+                return
             dlc.dlc_outer_cycle(theta, mom, theta_L if bc else inp.theta_L, grouped, first, weights, codes, cb, rng,
                                 ws, broadcast=bc, quantize_stream=qs, merge_stream=merge_stream, two_lanes=lanes)
         for _ in range(warmup):
@@ -329,13 +334,13 @@ def native_cycle(key, device, reps=5, warmup=2):
         b = (24 + 10 * k + (4 + 4 * k if bc else 0)) * n_params
         out[name] = dict(cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3), hbm_gbps=b / (ms_ * 1e-3) / 1e9,
                          bytes_per_param=b // n_params)
-    # the two-lane cycle captured once in a HIP graph and replayed: no host launch cost
-    graph, side, other = torch.cuda.CUDAGraph(), torch.cuda.Stream(), torch.cuda.Stream()
+    # the three-lane cycle captured once in a HIP graph and replayed: no host launch cost
+    graph, side, others = torch.cuda.CUDAGraph(), torch.cuda.Stream(), [torch.cuda.Stream(), torch.cuda.Stream()]
     side.wait_stream(qs)
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            dlc.dlc_outer_cycle(theta, mom, inp.theta_L, grouped, first, weights, codes, cb, rng, ws,
-                                quantize_stream=side, merge_stream=other, two_lanes=True)
+            dlc.dlc_outer_cycle_lanes(theta, mom, inp.theta_L, grouped, first, weights, codes, cb, rng, ws,
+                                      [side] + others)
     qs.wait_stream(side)
     for _ in range(warmup):
         graph.replay()
@@ -350,8 +355,8 @@ def native_cycle(key, device, reps=5, warmup=2):
         ts.append(e0.elapsed_time(e1))
     ms_ = statistics.median(ts)
     b = (24 + 10 * k) * n_params
-    out["two_lanes_graph"] = dict(cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3),
-                                  hbm_gbps=b / (ms_ * 1e-3) / 1e9, bytes_per_param=b // n_params)
+    out["three_lanes_graph"] = dict(cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3),
+                                    hbm_gbps=b / (ms_ * 1e-3) / 1e9, bytes_per_param=b // n_params)
     out["workload"] = cfg.title
     out["fragments"] = cfg.n_fragments
     return out

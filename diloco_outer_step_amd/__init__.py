@@ -27,6 +27,7 @@ DLC_RANGE_GIVEN = 1
 DLC_BROADCAST = 2
 DLC_TWO_LANES = 4
 DLC_MAX_LEARNERS = 64
+DLC_MAX_LANES = 8
 DLC_N_BUCKETS = 256
 DLC_ALIGN_ELEMS = 64
 DLC_RANGE_FIELDS = 4
@@ -34,7 +35,7 @@ DLC_RANGE_FIELDS = 4
 EXPORTED = (
     "dlc_fragment_plan", "dlc_workspace_bytes", "dlc_quantize_range", "dlc_quantize_encode",
     "dlc_quantize", "dlc_quantize_bases", "dlc_merge_outer_step", "dlc_merge_weights", "dlc_broadcast",
-    "dlc_cycle_workspace_bytes", "dlc_outer_cycle", "dlc_ring_workspace_bytes", "dlc_ring_outer_step",
+    "dlc_cycle_workspace_bytes", "dlc_outer_cycle", "dlc_outer_cycle_lanes", "dlc_ring_workspace_bytes", "dlc_ring_outer_step",
     "dlc_rda_workspace_bytes", "dlc_rda_outer_step", "dlc_last_error", "dlc_version",
 )
 
@@ -79,6 +80,8 @@ def _load() -> ctypes.CDLL:
         "dlc_cycle_workspace_bytes": [i32, tp, vp, i32, ctypes.POINTER(sz)],
         "dlc_outer_cycle": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, ctypes.c_double, ctypes.c_double,
                             u32, vp, sz, vp, vp],
+        "dlc_outer_cycle_lanes": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, ctypes.c_double,
+                                  ctypes.c_double, u32, vp, sz, vp, i32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -336,6 +339,23 @@ def dlc_outer_cycle(theta_g, momentum, theta_L, tensors, fragment_first, weights
                                 _ptr(range_out), float(lr), float(beta),
                                 (DLC_BROADCAST if broadcast else 0) | (DLC_TWO_LANES if two_lanes else 0),
                                 _ptr(workspace), workspace.numel(), qs, ms))
+
+
+def dlc_outer_cycle_lanes(theta_g, momentum, theta_L, tensors, fragment_first, weights, codes, codebook, range_out,
+                          workspace, streams, lr=0.7, beta=0.9, broadcast=False):
+    """The fragment cycle with the non-empty fragments taking the given streams in
+    turn (workspace of len(streams) times dlc_cycle_workspace_bytes)."""
+    k = theta_L.shape[0]
+    nf = len(fragment_first) - 1
+    arr, _ = _tensors(tensors)
+    _fb, fp = _fragments(fragment_first)
+    w = (ctypes.c_double * (nf * k))(*[float(x) for row in weights for x in row])
+    ss = (ctypes.c_void_p * max(1, len(streams)))(*[_stream(s).value for s in streams])
+    _check(_lib.dlc_outer_cycle_lanes(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k,
+                                      ctypes.cast(w, ctypes.c_void_p), arr, fp, nf, _ptr(codes), _ptr(codebook),
+                                      _ptr(range_out), float(lr), float(beta), DLC_BROADCAST if broadcast else 0,
+                                      _ptr(workspace), workspace.numel(), ctypes.cast(ss, ctypes.c_void_p),
+                                      len(streams)))
 
 
 def outputs_for(n_learners: int, learner_stride: int, n_tensors: int, device="cuda"):

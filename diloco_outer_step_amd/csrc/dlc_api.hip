@@ -441,6 +441,100 @@ int32_t check_fragments(const dlc_tensor* tensors, const int32_t* fragment_first
   return DLC_OK;
 }
 
+// One event recorded on `from` and waited on by `to`, created and destroyed here
+// (a capture on `from` extends to `to` through it).
+hipError_t order_after(hipStream_t from, hipStream_t to) {
+  hipEvent_t ev;
+  hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventRecord(ev, from);
+  if (e == hipSuccess) e = hipStreamWaitEvent(to, ev, 0);
+  if (e == hipSuccess) e = hipEventDestroy(ev);
+  return e;
+}
+
+// The fragment cycle.  n_lanes == 0: quantize calls on quantize_stream, merges
+// (and broadcasts) on merge_stream, each merge after its fragment's quantization
+// through an event.  n_lanes >= 1: the non-empty fragments take the lanes in turn,
+// each lane with its own stream and its own equal share of the workspace, and a
+// fragment's quantize, merge and broadcast all run on its lane.
+int32_t outer_cycle(float* theta_global, float* momentum, float* theta_learners, int64_t learner_stride,
+                    int32_t n_learners, const double* weights, const dlc_tensor* tensors,
+                    const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
+                    float* range, double lr, double beta, bool broadcast, void* workspace, size_t workspace_bytes,
+                    hipStream_t quantize_stream, hipStream_t merge_stream, const hipStream_t* lane_streams,
+                    int32_t n_lanes) {
+  if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
+  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
+    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
+  int32_t rc = check_fragments(tensors, fragment_first, n_fragments);
+  if (rc != DLC_OK) return rc;
+  const int32_t n_tensors = fragment_first[n_fragments];
+  rc = check_tensors(tensors, n_tensors, learner_stride, true);
+  if (rc != DLC_OK) return rc;
+  if (!weights) return fail(DLC_ERR_INVALID_ARGUMENT, "weights is NULL");
+  const bool lanes = n_lanes > 0;
+  const size_t share = lanes ? (workspace_bytes / (size_t)n_lanes) & ~size_t(255) : workspace_bytes;
+  // Every check before anything is enqueued: per-fragment merge arguments and quorum,
+  // quantize setup (workspace size) for every non-empty fragment.
+  std::vector<dlc::MergeArgs> margs(n_fragments);
+  std::vector<Common> qc(n_fragments);
+  std::vector<int32_t> lane(n_fragments, 0);
+  std::vector<uint8_t> present(n_learners);
+  int32_t busy = 0;
+  for (int32_t f = 0; f < n_fragments; ++f) {
+    const int32_t n = fragment_first[f + 1] - fragment_first[f];
+    if (n == 0) continue;
+    lane[f] = lanes ? busy++ % n_lanes : 0;
+    const double* w = weights + (size_t)f * n_learners;
+    rc = prepare_merge(margs[f], theta_global, momentum, codes, learner_stride, n_learners, codebook, w, lr, beta);
+    if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
+    for (int32_t i = 0; i < n_learners; ++i) present[i] = w[i] > 0.0 ? 1 : 0;
+    void* lane_ws = workspace == nullptr ? nullptr : static_cast<char*>(workspace) + (size_t)lane[f] * share;
+    rc = setup_quant(qc[f], theta_global, theta_learners, learner_stride, n_learners, present.data(),
+                     tensors + fragment_first[f], n, lane_ws, share, lanes ? lane_streams[lane[f]] : quantize_stream,
+                     fragment_first[f], n_tensors);
+    if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
+    qc[f].args.range = reinterpret_cast<float4*>(range);
+    qc[f].args.codes = codes;
+    qc[f].args.codebook = codebook;
+  }
+  hipError_t e = hipSuccess;
+  // the other lanes start after the work already on the first lane's stream (this
+  // also joins them to a capture of that stream)
+  for (int32_t l = 1; l < n_lanes && e == hipSuccess; ++l) e = order_after(lane_streams[0], lane_streams[l]);
+  if (e != hipSuccess) return hip_fail(e, "cycle event");
+  for (int32_t f = 0; f < n_fragments; ++f) {
+    const int32_t n = fragment_first[f + 1] - fragment_first[f];
+    if (n == 0) continue;
+    rc = run_range(qc[f]);
+    if (rc == DLC_OK) rc = run_encode(qc[f]);
+    if (rc != DLC_OK) return rc;
+    hipStream_t ms = merge_stream;
+    if (lanes) {
+      ms = lane_streams[lane[f]];
+    } else {
+      // merge of this fragment after its quantization; the next fragment's
+      // quantization proceeds on the quantize stream meanwhile
+      e = order_after(quantize_stream, merge_stream);
+      if (e != hipSuccess) return hip_fail(e, "cycle event");
+    }
+    rc = run_merge(margs[f], tensors + fragment_first[f], n, fragment_first[f], n_tensors, ms);
+    if (rc == DLC_OK && broadcast)
+      rc = run_broadcast(theta_global, theta_learners, learner_stride, n_learners, nullptr,
+                         tensors + fragment_first[f], n, ms);
+    if (rc != DLC_OK) return rc;
+  }
+  // the streams join: any one of them completes the cycle
+  if (lanes) {
+    for (int32_t l = 1; l < n_lanes && e == hipSuccess; ++l) e = order_after(lane_streams[l], lane_streams[0]);
+    for (int32_t l = 1; l < n_lanes && e == hipSuccess; ++l) e = order_after(lane_streams[0], lane_streams[l]);
+  } else {
+    e = order_after(merge_stream, quantize_stream);
+  }
+  if (e != hipSuccess) return hip_fail(e, "cycle event");
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -635,100 +729,27 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
                         float* range, double lr, double beta, uint32_t flags, void* workspace,
                         size_t workspace_bytes, void* quantize_stream, void* merge_stream) {
   if ((flags & ~(DLC_BROADCAST | DLC_TWO_LANES)) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
-  if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
-  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
-    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
-  int32_t rc = check_fragments(tensors, fragment_first, n_fragments);
-  if (rc != DLC_OK) return rc;
-  const int32_t n_tensors = fragment_first[n_fragments];
-  rc = check_tensors(tensors, n_tensors, learner_stride, true);
-  if (rc != DLC_OK) return rc;
-  if (!weights) return fail(DLC_ERR_INVALID_ARGUMENT, "weights is NULL");
-  // Two lanes: the non-empty fragments alternate between the two streams, each lane
-  // with its own half of the workspace, and a fragment's quantize, merge and send
-  // back all run on its lane.
+  const hipStream_t qs = static_cast<hipStream_t>(quantize_stream), ms = static_cast<hipStream_t>(merge_stream);
+  const hipStream_t two[2] = {qs, ms};
   const bool lanes = (flags & DLC_TWO_LANES) != 0;
-  const size_t half = lanes ? (workspace_bytes / 2) & ~size_t(255) : workspace_bytes;
-  // Every check before anything is enqueued: per-fragment merge arguments and quorum,
-  // quantize setup (workspace size) for every non-empty fragment.
-  std::vector<dlc::MergeArgs> margs(n_fragments);
-  std::vector<Common> qc(n_fragments);
-  std::vector<int32_t> lane(n_fragments, 0);
-  std::vector<uint8_t> present(n_learners);
-  int32_t busy = 0;
-  for (int32_t f = 0; f < n_fragments; ++f) {
-    const int32_t n = fragment_first[f + 1] - fragment_first[f];
-    if (n == 0) continue;
-    lane[f] = lanes ? busy++ % 2 : 0;
-    const double* w = weights + (size_t)f * n_learners;
-    rc = prepare_merge(margs[f], theta_global, momentum, codes, learner_stride, n_learners, codebook, w, lr, beta);
-    if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
-    for (int32_t i = 0; i < n_learners; ++i) present[i] = w[i] > 0.0 ? 1 : 0;
-    void* lane_ws = workspace == nullptr ? nullptr : static_cast<char*>(workspace) + (size_t)lane[f] * half;
-    rc = setup_quant(qc[f], theta_global, theta_learners, learner_stride, n_learners, present.data(),
-                     tensors + fragment_first[f], n, lane_ws, half, lane[f] == 0 ? quantize_stream : merge_stream,
-                     fragment_first[f], n_tensors);
-    if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
-    qc[f].args.range = reinterpret_cast<float4*>(range);
-    qc[f].args.codes = codes;
-    qc[f].args.codebook = codebook;
-  }
-  hipStream_t qs = static_cast<hipStream_t>(quantize_stream), ms = static_cast<hipStream_t>(merge_stream);
-  if (lanes) {
-    // the second lane starts after the work already on the quantize stream (this
-    // also joins it to a capture of the quantize stream)
-    hipEvent_t fork;
-    hipError_t e = hipEventCreateWithFlags(&fork, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventRecord(fork, qs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ms, fork, 0);
-    if (e == hipSuccess) e = hipEventDestroy(fork);
-    if (e != hipSuccess) return hip_fail(e, "cycle event");
-  }
-  for (int32_t f = 0; f < n_fragments; ++f) {
-    const int32_t n = fragment_first[f + 1] - fragment_first[f];
-    if (n == 0) continue;
-    rc = run_range(qc[f]);
-    if (rc == DLC_OK) rc = run_encode(qc[f]);
-    if (rc != DLC_OK) return rc;
-    if (lanes) {
-      hipStream_t ls = lane[f] == 0 ? qs : ms;
-      rc = run_merge(margs[f], tensors + fragment_first[f], n, fragment_first[f], n_tensors, ls);
-      if (rc == DLC_OK && (flags & DLC_BROADCAST))
-        rc = run_broadcast(theta_global, theta_learners, learner_stride, n_learners, nullptr,
-                           tensors + fragment_first[f], n, ls);
-      if (rc != DLC_OK) return rc;
-      continue;
-    }
-    // merge of this fragment after its quantization; the next fragment's
-    // quantization proceeds on the quantize stream meanwhile
-    hipEvent_t done;
-    hipError_t e = hipEventCreateWithFlags(&done, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventRecord(done, qs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ms, done, 0);
-    if (e == hipSuccess) e = hipEventDestroy(done);
-    if (e != hipSuccess) return hip_fail(e, "cycle event");
-    rc = run_merge(margs[f], tensors + fragment_first[f], n, fragment_first[f], n_tensors, ms);
-    if (rc != DLC_OK) return rc;
-    if (flags & DLC_BROADCAST) {
-      rc = run_broadcast(theta_global, theta_learners, learner_stride, n_learners, nullptr,
-                         tensors + fragment_first[f], n, ms);
-      if (rc != DLC_OK) return rc;
-    }
-  }
-  // the streams join: either one completes the cycle
-  hipEvent_t end;
-  hipError_t e = hipEventCreateWithFlags(&end, hipEventDisableTiming);
-  if (e == hipSuccess) e = hipEventRecord(end, ms);
-  if (e == hipSuccess) e = hipStreamWaitEvent(qs, end, 0);
-  if (e == hipSuccess) e = hipEventDestroy(end);
-  if (e == hipSuccess && lanes) {
-    e = hipEventCreateWithFlags(&end, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventRecord(end, qs);
-    if (e == hipSuccess) e = hipStreamWaitEvent(ms, end, 0);
-    if (e == hipSuccess) e = hipEventDestroy(end);
-  }
-  if (e != hipSuccess) return hip_fail(e, "cycle event");
-  return ok();
+  return outer_cycle(theta_global, momentum, theta_learners, learner_stride, n_learners, weights, tensors,
+                     fragment_first, n_fragments, codes, codebook, range, lr, beta, (flags & DLC_BROADCAST) != 0,
+                     workspace, workspace_bytes, qs, ms, two, lanes ? 2 : 0);
+}
+
+int32_t dlc_outer_cycle_lanes(float* theta_global, float* momentum, float* theta_learners, int64_t learner_stride,
+                              int32_t n_learners, const double* weights, const dlc_tensor* tensors,
+                              const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
+                              float* range, double lr, double beta, uint32_t flags, void* workspace,
+                              size_t workspace_bytes, void* const* streams, int32_t n_lanes) {
+  if ((flags & ~DLC_BROADCAST) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
+  if (n_lanes < 1 || n_lanes > DLC_MAX_LANES) return fail(DLC_ERR_INVALID_ARGUMENT, "n_lanes must be in [1, 8]");
+  if (!streams) return fail(DLC_ERR_INVALID_ARGUMENT, "streams is NULL");
+  hipStream_t lane_streams[DLC_MAX_LANES];
+  for (int32_t l = 0; l < n_lanes; ++l) lane_streams[l] = static_cast<hipStream_t>(streams[l]);
+  return outer_cycle(theta_global, momentum, theta_learners, learner_stride, n_learners, weights, tensors,
+                     fragment_first, n_fragments, codes, codebook, range, lr, beta, (flags & DLC_BROADCAST) != 0,
+                     workspace, workspace_bytes, lane_streams[0], lane_streams[0], lane_streams, n_lanes);
 }
 
 int32_t dlc_merge_weights(int32_t n_learners, const double* tokens, const double* arrival, int32_t quorum,

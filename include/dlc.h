@@ -73,6 +73,7 @@ extern "C" {
 #define DLC_TWO_LANES 4u
 
 #define DLC_MAX_LEARNERS 64
+#define DLC_MAX_LANES 8
 #define DLC_N_BUCKETS 256
 #define DLC_ALIGN_ELEMS 64
 #define DLC_RANGE_FIELDS 4
@@ -255,6 +256,32 @@ int32_t dlc_outer_cycle(float* theta_global, float* momentum, float* theta_learn
                         const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
                         float* range, double lr, double beta, uint32_t flags, void* workspace,
                         size_t workspace_bytes, void* quantize_stream, void* merge_stream);
+
+/*
+ * dlc_outer_cycle_lanes -- the same cycle (same arguments, same results) with the
+ * non-empty fragments taking n_lanes streams in turn: fragment j (counting
+ * non-empty fragments only) runs its quantize, merge and send back on
+ * streams[j % n_lanes], with that lane's share of the workspace.  Lanes pay off
+ * when fragments are small (kernels of a few tens of microseconds): several
+ * fragments in flight keep the device busy.  Lanes beyond the device's hardware
+ * queues share queues and serialize.
+ *   flags       0 or DLC_BROADCAST
+ *   workspace   >= n_lanes * dlc_cycle_workspace_bytes(...) bytes, split into
+ *               n_lanes equal shares (each rounded down to 256 bytes)
+ *   streams     host [n_lanes] HIP streams (a stream may repeat)
+ *   n_lanes     1..DLC_MAX_LANES; 1 runs everything on streams[0]
+ * Lanes 1.. first wait for the work already enqueued on streams[0]; at the end
+ * streams[0] waits for every lane and every lane for streams[0], so synchronizing
+ * any one of them completes the cycle.  The call can be captured in a HIP graph
+ * on streams[0] (the other lanes join the capture through the call's events).
+ * DLC_TWO_LANES in dlc_outer_cycle is this call with the streams
+ * {quantize_stream, merge_stream}.
+ */
+int32_t dlc_outer_cycle_lanes(float* theta_global, float* momentum, float* theta_learners, int64_t learner_stride,
+                              int32_t n_learners, const double* weights, const dlc_tensor* tensors,
+                              const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
+                              float* range, double lr, double beta, uint32_t flags, void* workspace,
+                              size_t workspace_bytes, void* const* streams, int32_t n_lanes);
 
 /*
  * dlc_merge_weights -- which learners a fragment's merge takes, and their weights

@@ -41,7 +41,8 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ("DLC_OK", "DLC_ERR_INVALID_ARGUMENT", "DLC_ERR_ALIGNMENT", "DLC_ERR_NO_QUORUM",
                  "DLC_ERR_WORKSPACE", "DLC_ERR_HIP", "DLC_MAX_LEARNERS", "DLC_N_BUCKETS",
-                 "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS", "DLC_RANGE_GIVEN", "DLC_BROADCAST", "DLC_TWO_LANES"):
+                 "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS", "DLC_RANGE_GIVEN", "DLC_BROADCAST", "DLC_TWO_LANES",
+                 "DLC_MAX_LANES"):
         m = re.search(rf"#define {name} \(?(-?\d+)u?\)?", text)
         assert m and int(m.group(1)) == getattr(dlc, name), name
 
@@ -129,6 +130,26 @@ def cycle(k=2, spec=((0, 0, 4096), (4096, 4096, 64)), first=(0, 1, 2), stride=81
     return L.dlc_outer_cycle(FAKE, FAKE, FAKE, stride, k, ctypes.cast(w, ctypes.c_void_p), arr,
                              ctypes.cast(fb, ctypes.c_void_p), len(first) - 1, codes, FAKE, FAKE, 0.7, 0.9, flags,
                              FAKE, ws_bytes, None, None)
+
+
+def cycle_lanes(n_lanes=3, streams=True, flags=0, ws_bytes=1 << 30, weights=((1.0, 1.0), (1.0, 1.0))):
+    L = dlc._lib
+    k, spec, first = 2, ((0, 0, 4096), (4096, 4096, 64)), (0, 1, 2)
+    arr, _ = dlc._tensors(spec)
+    fb = (ctypes.c_int32 * len(first))(*first)
+    w = (ctypes.c_double * (len(weights) * k))(*[x for row in weights for x in row])
+    ss = (ctypes.c_void_p * 9)()  # null streams: the calls below fail before anything is enqueued
+    return L.dlc_outer_cycle_lanes(FAKE, FAKE, FAKE, 8192, k, ctypes.cast(w, ctypes.c_void_p), arr,
+                                   ctypes.cast(fb, ctypes.c_void_p), len(first) - 1, FAKE, FAKE, FAKE, 0.7, 0.9,
+                                   flags, FAKE, ws_bytes, ctypes.cast(ss, ctypes.c_void_p) if streams else None,
+                                   n_lanes)
+
+
+def lanes_ws_short():
+    """Workspace for two lanes handed to a call with three."""
+    arr, _ = dlc._tensors(((0, 0, 4096), (4096, 4096, 64)))
+    need = dlc.dlc_cycle_workspace_bytes(2, ((0, 0, 4096), (4096, 4096, 64)), (0, 1, 2))
+    return cycle_lanes(n_lanes=3, ws_bytes=2 * need)
 
 
 def merge(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), lr=0.7, beta=0.9, flags=0, theta=FAKE):
@@ -243,6 +264,13 @@ def test_rda_and_ring_workspace_sizes():
     (lambda: cycle(codes=FAKE + 32), dlc.DLC_ERR_ALIGNMENT),
     (lambda: cycle(first=(0, 2, 1)), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: cycle(spec=((0, 0, 4096), (0, 4096, 64))), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_lanes(n_lanes=0), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_lanes(n_lanes=9), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_lanes(streams=False), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_lanes(flags=4), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: cycle_lanes(weights=((1.0, 1.0), (0.0, 0.0))), dlc.DLC_ERR_NO_QUORUM),
+    (lambda: cycle_lanes(ws_bytes=64), dlc.DLC_ERR_WORKSPACE),
+    (lambda: lanes_ws_short(), dlc.DLC_ERR_WORKSPACE),
 ])
 def test_argument_errors(call, code):
     assert call() == code

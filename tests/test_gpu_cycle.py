@@ -4,8 +4,9 @@ over every fragment with overlapped streams (dlc_outer_cycle).
 * broadcast: bit-exact copies, for every padded row count the kernel is built
   for (4, 8, 12, 16 rows) and the run-time row count, ragged tails, row subsets;
 * cycle: bit-exact against the same calls made fragment by fragment, on one and
-  on two streams; against the oracle's cycle with the parity bar of
-  tests/parity.py; the 135M set's 24-fragment cycle with send-back.
+  on two streams, on two lanes, and through dlc_outer_cycle_lanes on 1, 3 and 4
+  lanes; against the oracle's cycle with the parity bar of tests/parity.py; the
+  135M set's 24-fragment cycle with send-back.
 """
 import numpy as np
 import pytest
@@ -68,16 +69,22 @@ def cycle_inputs(seed, k, sizes, n_fragments, absent=True):
     return theta, mom, theta_L, grouped, first, weights
 
 
-def run_cycle(theta, mom, theta_L, grouped, first, weights, broadcast, two_streams, two_lanes=False):
+def run_cycle(theta, mom, theta_L, grouped, first, weights, broadcast, two_streams, two_lanes=False, lanes=None):
+    """lanes: a list of streams (None = the current stream) for dlc_outer_cycle_lanes."""
     k, stride = theta_L.shape
     theta, mom, theta_L = theta.clone(), mom.clone(), theta_L.clone()
     codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), DEV)
-    need = dlc.dlc_cycle_workspace_bytes(k, grouped, first) * (2 if two_lanes else 1)
+    copies = len(lanes) if lanes is not None else 2 if two_lanes else 1
+    need = dlc.dlc_cycle_workspace_bytes(k, grouped, first) * copies
     ws = torch.empty(max(256, need), dtype=torch.uint8, device=DEV)
     qs = torch.cuda.current_stream()
-    ms = torch.cuda.Stream() if two_streams else qs
-    dlc.dlc_outer_cycle(theta, mom, theta_L, grouped, first, weights, codes, cb, rng, ws, broadcast=broadcast,
-                        quantize_stream=qs, merge_stream=ms, two_lanes=two_lanes)
+    if lanes is not None:
+        dlc.dlc_outer_cycle_lanes(theta, mom, theta_L, grouped, first, weights, codes, cb, rng, ws,
+                                  [qs if s is None else s for s in lanes], broadcast=broadcast)
+    else:
+        ms = torch.cuda.Stream() if two_streams else qs
+        dlc.dlc_outer_cycle(theta, mom, theta_L, grouped, first, weights, codes, cb, rng, ws, broadcast=broadcast,
+                            quantize_stream=qs, merge_stream=ms, two_lanes=two_lanes)
     torch.cuda.synchronize()
     return dict(theta=theta, momentum=mom, theta_L=theta_L, codes=codes, codebook=cb, range=rng)
 
@@ -129,6 +136,21 @@ def test_cycle_equals_fragment_by_fragment(two_streams, two_lanes, broadcast):
     assert_same(a, b, args[5], args[3], args[4])
 
 
+@pytest.mark.parametrize("n_lanes,repeat", [(1, False), (3, False), (4, False), (3, True)])
+@pytest.mark.parametrize("broadcast", [False, True])
+def test_lanes_equal_fragment_by_fragment(n_lanes, repeat, broadcast):
+    """dlc_outer_cycle_lanes on 1, 3 and 4 streams, and on three lanes of which two
+    share a stream."""
+    sizes = RAGGED + [4096] * 12 + [64 * 3000 + 7] * 3 + [1 << 18]
+    args = cycle_inputs(9, 4, sizes, 9)
+    streams = [None] + [torch.cuda.Stream() for _ in range(n_lanes - 1)]
+    if repeat:
+        streams[2] = streams[1]
+    a = run_cycle(*args, broadcast=broadcast, two_streams=False, lanes=streams)
+    b = run_sequential(*args, broadcast=broadcast)
+    assert_same(a, b, args[5], args[3], args[4])
+
+
 def test_cycle_against_oracle_with_empty_fragment_and_absent_learners():
     sizes = [5000, 4096 * 3 + 1, 777, 64 * 100, 9000]
     theta, mom, theta_L, grouped, first, weights = cycle_inputs(11, 4, sizes, 7)  # 7 > 5 tensors: empty fragments
@@ -165,3 +187,5 @@ def test_c2_cycle_with_send_back_equals_sequential():
     assert_same(a, b, weights, grouped, first)
     c = run_cycle(*args, broadcast=True, two_streams=True, two_lanes=True)
     assert_same(c, b, weights, grouped, first)
+    d = run_cycle(*args, broadcast=True, two_streams=False, lanes=[None, torch.cuda.Stream(), torch.cuda.Stream()])
+    assert_same(d, b, weights, grouped, first)

@@ -53,10 +53,12 @@ def test_captured_step_replays_the_eager_step():
         assert torch.equal(th, th_e) and torch.equal(mo, mo_e), rep
 
 
-@pytest.mark.parametrize("two_lanes", [False, True])
-def test_captured_cycle_replays_the_eager_cycle(two_lanes):
+@pytest.mark.parametrize("mode", ["two_streams", "two_lanes", "three_lanes"])
+def test_captured_cycle_replays_the_eager_cycle(mode):
     """A whole fragment cycle on two streams (the second joins the capture through
-    the cycle's own events), captured once and replayed."""
+    the cycle's own events), on two lanes, and on three lanes through
+    dlc_outer_cycle_lanes, captured once and replayed."""
+    two_lanes = mode == "two_lanes"
     sizes = [4096] * 6 + [64 * 1000 + 5] * 3 + [1 << 17, 777]
     cfg = workloads.custom("graph_cycle", sizes, 4)
     inp = workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV)
@@ -64,7 +66,7 @@ def test_captured_cycle_replays_the_eager_cycle(two_lanes):
     frag, _ = dlc.dlc_fragment_plan(sizes, 5)
     grouped, first, _ = dlc.group_by_fragment(inp.tensors, frag, 5)
     weights = [list(inp.weights)] * 5
-    need = dlc.dlc_cycle_workspace_bytes(k, grouped, first) * 2
+    need = dlc.dlc_cycle_workspace_bytes(k, grouped, first) * 3
 
     def buffers():
         codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), DEV)
@@ -72,19 +74,26 @@ def test_captured_cycle_replays_the_eager_cycle(two_lanes):
         return codes, cb, rng, ws, inp.theta_g.clone(), inp.momentum.clone(), inp.theta_L.clone()
 
     codes_e, cb_e, rng_e, ws_e, th_e, mo_e, tl_e = buffers()
-    other = torch.cuda.Stream()
-    dlc.dlc_outer_cycle(th_e, mo_e, tl_e, grouped, first, weights, codes_e, cb_e, rng_e, ws_e, broadcast=True,
-                        quantize_stream=torch.cuda.current_stream(), merge_stream=other, two_lanes=two_lanes)
+
+    def cycle(th, mo, tl, codes, cb, rng, ws, first_stream, others):
+        if mode == "three_lanes":
+            dlc.dlc_outer_cycle_lanes(th, mo, tl, grouped, first, weights, codes, cb, rng, ws,
+                                      [first_stream] + others, broadcast=True)
+        else:
+            dlc.dlc_outer_cycle(th, mo, tl, grouped, first, weights, codes, cb, rng, ws, broadcast=True,
+                                quantize_stream=first_stream, merge_stream=others[0], two_lanes=two_lanes)
+
+    cycle(th_e, mo_e, tl_e, codes_e, cb_e, rng_e, ws_e, torch.cuda.current_stream(),
+          [torch.cuda.Stream(), torch.cuda.Stream()])
     torch.cuda.synchronize()
 
     codes, cb, rng, ws, th, mo, tl = buffers()
     graph = torch.cuda.CUDAGraph()
-    side, other2 = torch.cuda.Stream(), torch.cuda.Stream()
+    side, others = torch.cuda.Stream(), [torch.cuda.Stream(), torch.cuda.Stream()]
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
-            dlc.dlc_outer_cycle(th, mo, tl, grouped, first, weights, codes, cb, rng, ws, broadcast=True,
-                                quantize_stream=side, merge_stream=other2, two_lanes=two_lanes)
+            cycle(th, mo, tl, codes, cb, rng, ws, side, others)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     for rep in range(3):
