@@ -170,7 +170,8 @@ def test_rda_full_1b_set_sampled_tensors():
     theta0, mom0 = inp.theta_g.clone(), inp.momentum.clone()
     gpu = gpu_rda(inp)
     sizes = sorted((n, t) for t, (_, _, n) in enumerate(inp.tensors))
-    picks = sorted({sizes[0][1], sizes[len(sizes) // 2][1], max((t for n, t in sizes if n <= 20_000_000))})
+    # the smallest tensor, the median one and the largest below 20M elements
+    picks = sorted({sizes[0][1], sizes[len(sizes) // 2][1], max((n, t) for n, t in sizes if n <= 20_000_000)[1]})
     w_hat = oracle.normalize_weights(inp.weights)
     present = [i for i, w in enumerate(inp.weights) if w > 0]
     for t in picks:

@@ -4,6 +4,8 @@ against the CPU oracle's ring_outer_step.
 * one rank: bit-identical to the star path (dlc_quantize + a one-learner merge);
 * constant chunks (every message lossless): bit-identical to the oracle,
   including the fp32 ring-order sums and the division by K;
+* the 1B set at K = 8, every tensor in one call, sampled tensors against the
+  oracle with the bar below;
 * Gaussian pseudo-gradients (K up to 16): the GPU's codebooks may differ from
   the oracle's by an ulp, which can move a later hop's code to the neighbouring
   bucket; that chunk's later sums, ranges and codes then differ too (the ring
@@ -19,6 +21,7 @@ import torch
 
 import diloco_outer_step_amd as dlc
 import oracle
+import workloads
 
 pytestmark = pytest.mark.gpu
 
@@ -85,20 +88,14 @@ def test_constant_chunks_bit_exact(k):
         np.testing.assert_array_equal(host(mo)[o:o + n], orc["momentum"][o:o + n])
 
 
-@pytest.mark.parametrize("k", [2, 4, 8, 16])
-def test_gaussian_against_oracle(k):
-    sizes = [64 * 300 + 9, 4096 * 8, 50000]
-    tensors, stride = packed(sizes)
-    g = torch.Generator(device=DEV)
-    g.manual_seed(10 + k)
-    theta = torch.randn(stride, generator=g, device=DEV) * 0.02
-    mom = torch.randn(stride, generator=g, device=DEV) * 1e-3
-    theta_L = torch.stack([theta - torch.randn(stride, generator=g, device=DEV) * 1e-3 for _ in range(k)])
-    th, mo = gpu_ring(theta, mom, theta_L, tensors)
-    orc = oracle.ring_outer_step(host(theta), host(mom), host(theta_L), stride, tensors, LR, BETA)
-    th_g, th_o = host(th).astype(np.float64), orc["theta"].astype(np.float64)
+def check_against_oracle(th_g, orc, theta, theta_L, tensors, k, t_ids=None):
+    """The ring parity bar, per tensor (o, lo, n) of `tensors` (GPU and oracle
+    results at the same offsets): returns (diverged chunks, chunks).  t_ids: the
+    oracle's tensor index of each entry (default: its position)."""
+    th_g, th_o = th_g.astype(np.float64), orc["theta"].astype(np.float64)
     diverged = chunks = 0
-    for t, (o, lo, n) in enumerate(tensors):
+    for j, (o, lo, n) in enumerate(tensors):
+        t = j if t_ids is None else t_ids[j]
         wd = max(float(q["wd"]) for (tt, _, _, _, q) in orc["messages"] if tt == t)
         for a, b in oracle.ring_chunks(n, k):
             if b <= a:
@@ -113,12 +110,59 @@ def test_gaussian_against_oracle(k):
                 diverged += 1
             assert d.max() <= LR * (1 + BETA) * 2.0 * wd, f"tensor {t} chunk [{a}, {b}): max |dtheta| {d.max():.3e}"
         # both rings are equally far from the exact mean of the pseudo-gradients
-        exact = np.mean([host(theta)[o:o + n].astype(np.float64)
-                         - host(theta_L)[r, lo:lo + n].astype(np.float64) for r in range(k)], 0)
-        ref = host(theta)[o:o + n].astype(np.float64)
+        exact = np.mean([theta[o:o + n].astype(np.float64) - theta_L[r, lo:lo + n].astype(np.float64)
+                         for r in range(k)], 0)
+        ref = theta[o:o + n].astype(np.float64)
         g_gpu = (ref - th_g[o:o + n]) / LR  # g + beta v_new, same v for both
         g_orc = (ref - th_o[o:o + n]) / LR
         e_gpu = np.sqrt(np.mean((g_gpu - g_orc) ** 2))
         assert e_gpu <= 0.05 * np.sqrt(np.mean(exact ** 2))
+    return diverged, chunks
+
+
+@pytest.mark.parametrize("k", [2, 4, 8, 16])
+def test_gaussian_against_oracle(k):
+    sizes = [64 * 300 + 9, 4096 * 8, 50000]
+    tensors, stride = packed(sizes)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(10 + k)
+    theta = torch.randn(stride, generator=g, device=DEV) * 0.02
+    mom = torch.randn(stride, generator=g, device=DEV) * 1e-3
+    theta_L = torch.stack([theta - torch.randn(stride, generator=g, device=DEV) * 1e-3 for _ in range(k)])
+    th, mo = gpu_ring(theta, mom, theta_L, tensors)
+    orc = oracle.ring_outer_step(host(theta), host(mom), host(theta_L), stride, tensors, LR, BETA)
+    diverged, chunks = check_against_oracle(host(th), orc, host(theta), host(theta_L), tensors, k)
     # divergence is the exception (none at all for K <= 8 on these inputs)
     assert diverged <= max(1, chunks // 10), f"{diverged} of {chunks} chunks diverged"
+
+
+@pytest.mark.slow
+def test_ring_full_1b_set_sampled_tensors():
+    """The ring over all 147 tensors of the 1B set at K = 8, in the launch layout
+    the bench times; sampled tensors against the oracle's ring over those tensors
+    alone (every message is one chunk of one tensor, so tensors are independent)."""
+    cfg = workloads.config("c3")
+    inp = workloads.fragment_inputs(cfg, list(range(len(cfg.tensors))), DEV)
+    k = inp.theta_L.shape[0]
+    theta0, mom0 = inp.theta_g.clone(), inp.momentum.clone()
+    th, mo = gpu_ring(inp.theta_g, inp.momentum, inp.theta_L, inp.tensors)
+    sizes = sorted((n, t) for t, (_, _, n) in enumerate(inp.tensors))
+    # the smallest tensor, the largest below 2M and the largest below 5M elements (2048, 512 x 2048, 2048^2)
+    picks = sorted({sizes[0][1], max((n, t) for n, t in sizes if n <= 2_000_000)[1],
+                    max((n, t) for n, t in sizes if n <= 5_000_000)[1]})
+    sub, stride = packed([inp.tensors[t][2] for t in picks])
+    th0 = np.zeros(stride, np.float32)
+    mo0 = np.zeros(stride, np.float32)
+    tl = np.zeros((k, stride), np.float32)
+    th_gpu = np.zeros(stride, np.float32)
+    for (o2, _, n), t in zip(sub, picks):
+        o, lo, _ = inp.tensors[t]
+        th0[o2:o2 + n] = host(theta0[o:o + n])
+        mo0[o2:o2 + n] = host(mom0[o:o + n])
+        tl[:, o2:o2 + n] = host(inp.theta_L[:, lo:lo + n])
+        th_gpu[o2:o2 + n] = host(th[o:o + n])
+    orc = oracle.ring_outer_step(th0, mo0, tl, stride, sub, LR, BETA)
+    diverged, chunks = check_against_oracle(th_gpu, orc, th0, tl, sub, k)
+    print(f"[ring c3] tensors {picks} ({[n for _, _, n in sub]} params, K = {k}): "
+          f"{diverged} of {chunks} chunks diverged", flush=True)
+    assert diverged <= max(1, chunks // 10)
