@@ -70,3 +70,52 @@ def test_single_base_equals_dlc_quantize():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+@pytest.mark.slow
+def test_stale_full_1b_set_sampled_tensors():
+    """The 1B set at K = 8, odd learners against an older theta, token weights with
+    one learner past the merge deadline, every tensor in one call as the bench
+    times it; sampled tensors against the oracle one by one (a tensor's results
+    depend on that tensor only)."""
+    from types import SimpleNamespace
+    cfg = workloads.config("c3")
+    inp = workloads.fragment_inputs(cfg, list(range(len(cfg.tensors))), DEV)
+    k, stride = inp.theta_L.shape
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    old = inp.theta_g - torch.randn(inp.theta_g.shape, generator=g, device=DEV) * 1e-3
+    bases = [inp.theta_g if i % 2 == 0 else old for i in range(k)]
+    tokens = [1000.0 * (i + 1) for i in range(k)]
+    arrival = [0.1 * i for i in range(k)]
+    arrival[3] = 5.0
+    weights, _ = dlc.dlc_merge_weights(tokens, arrival, k - 2, 0.5)
+    present = [1 if w > 0 else 0 for w in weights]
+    assert present == [1, 1, 1, 0, 1, 1, 1, 1]
+    codes, cb, rng = dlc.outputs_for(k, stride, len(inp.tensors), DEV)
+    ws = dlc.alloc_workspace(k, inp.tensors, DEV)
+    th, mo = inp.theta_g.clone(), inp.momentum.clone()
+    dlc.dlc_quantize_bases(bases, inp.theta_L, inp.tensors, codes, cb, rng, ws, present=present)
+    dlc.dlc_merge_outer_step(th, mo, codes, cb, weights, inp.tensors, cfg.lr, cfg.beta)
+    torch.cuda.synchronize()
+    sizes = sorted((n, t) for t, (_, _, n) in enumerate(inp.tensors))
+    # the smallest tensor, the median one and the largest below 5M elements
+    picks = sorted({sizes[0][1], sizes[len(sizes) // 2][1], max((n, t) for n, t in sizes if n <= 5_000_000)[1]})
+    for t in picks:
+        off, loff, n = inp.tensors[t]
+        sn = (n + 63) // 64 * 64
+        tl = np.zeros((k, sn), np.float32)
+        for i in range(k):
+            if present[i]:
+                tl[i, :n] = parity.host(inp.theta_L[i, loff:loff + n])
+        bs = [parity.host(b[off:off + n]) for b in bases]
+        orc = oracle.outer_step(parity.host(inp.theta_g[off:off + n]), parity.host(inp.momentum[off:off + n]), tl,
+                                sn, [(0, 0, n)], weights, present, cfg.lr, cfg.beta, bases=bs)
+        gc = torch.zeros((k, sn), dtype=torch.uint8)
+        gc[:, :n] = codes[:, loff:loff + n].cpu()
+        gpu = dict(codes=gc, codebook=cb[:, t:t + 1], range=rng[:, t:t + 1], theta=th[off:off + n],
+                   momentum=mo[off:off + n])
+        view = SimpleNamespace(theta_L=tl, tensors=[(0, 0, n)], weights=weights, present=present)
+        rep = parity.compare(gpu, orc, view, pinned=False)
+        print(f"[stale c3] tensor {t} ({n} params): flips {rep['flips']}, theta exact {rep['theta_exact']}/{n}",
+              flush=True)
