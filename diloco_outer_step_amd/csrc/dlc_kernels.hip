@@ -3,7 +3,7 @@
 // Three streaming passes over HBM per outer step, plus two small finalizers:
 //   k_stats     per-(learner, tensor) partial sum(d), sum(d^2) of d = Delta - shift, fp64
 //   k_range     per-(learner, tensor) mu, sigma -> {lo, hi, wd, mean} (fp64 -> fp32)
-//   k_encode    Delta -> clip -> bucket -> uint8 code (16-byte stores) + LDS histogram
+//   k_encode    Delta -> clip -> bucket -> uint8 code (256-byte runs per wave store) + LDS histogram
 //               of (count, fixed-point position sum) per bucket and learner
 //   k_codebook  per-(learner, tensor, bucket) mean of the clipped values -> fp32
 //   k_merge     dequantize K learners through fp64 LDS tables w_hat_i * codebook_i,
@@ -334,9 +334,9 @@ __global__ __launch_bounds__(kRangeThreads) void k_range(const QuantArgs a, cons
 // Histogram: one 64-bit LDS atomic per element adds the count unit and the
 // element's position inside its bucket as a fixed-point integer, see
 // EncodePar.  Integer sums make the histogram exact and independent of the order
-// of the atomics.  Codes of a full tile are packed 4 per dword in the load layout,
-// transposed through a per-wave LDS stage, and written with 16-byte stores: one
-// store instruction writes the wave's 1 KB of codes contiguously.
+// of the atomics.  Codes of a full tile are packed 4 per dword in the load layout
+// and stored as they are: each of a wave's four dword store instructions writes 256
+// consecutive bytes (whole cache lines), together the wave's 1 KB of codes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float uniform_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
