@@ -9,9 +9,11 @@ Importing this package fails loudly if the library has not been built
 from __future__ import annotations
 
 import ctypes
+import itertools
 import os
 from typing import Optional, Sequence, Tuple
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -106,10 +108,13 @@ def _check(rc: int) -> None:
 
 
 def _tensors(tensors: Sequence[Tuple[int, int, int]]):
-    arr = (_Tensor * max(1, len(tensors)))()
-    for i, (o, lo, n) in enumerate(tensors):
-        arr[i].offset, arr[i].loffset, arr[i].numel = int(o), int(lo), int(n)
-    return arr, len(tensors)
+    """dlc_tensor array of (offset, loffset, numel) triples: one int64 [n][3] array
+    viewed as the C structs (the ctypes array keeps that buffer alive)."""
+    n = len(tensors)
+    if n == 0:
+        return (_Tensor * 1)(), 0
+    a = np.fromiter(itertools.chain.from_iterable(tensors), dtype=np.int64, count=3 * n)
+    return (_Tensor * n).from_buffer(a), n
 
 
 def _ptr(t: Optional[torch.Tensor]):
