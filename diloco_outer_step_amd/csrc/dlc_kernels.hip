@@ -156,9 +156,10 @@ __device__ __forceinline__ void stats_accumulate(const float (&gv)[kVec], const 
 // items: theta_g first, then learners 0..KC-1; item i + kStatsRing - 1 is
 // requested while item i is accumulated.  KC + 1 is a multiple of the ring size,
 // so ring slots are compile-time constants across tiles.  A learner item beyond
-// k_count is a null request (zero-record buffer descriptor: no memory traffic)
-// and is not accumulated.  Every request is the same unconditional load through
-// a selected descriptor, so the compiler's wait counts stay exact.
+// k_count, and the look-ahead past the block's last tile, are null requests
+// (zero-record buffer descriptor: no memory traffic); they are not accumulated.
+// Every request is the same unconditional load through a selected descriptor, so
+// the compiler's wait counts stay exact.
 constexpr int kStatsRing = 3;
 
 template <int KC>
@@ -188,8 +189,8 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
   const int64_t n_full = (sp.end - sp.begin) / kTile;
   if (n_full > 0) {
     const int64_t last = sp.begin + (n_full - 1) * kTile;
-    auto request = [&](int item, int64_t base, float (&dst)[kVec]) {
-      const bool real = item == 0 ? has_base : item <= kc;
+    auto request = [&](int item, int64_t base, float (&dst)[kVec], bool live = true) {
+      const bool real = live && (item == 0 ? has_base : item <= kc);
       const float* src = (item == 0 || item > kc) ? tg : learner_row(a, item - 1, td);
       load_tile_rsrc(tile_rsrc(src + base, real), tid, dst);
     };
@@ -204,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void k_stats(const QuantArgs a, const Launc
         if (ip < kItems) {
           request(ip, base, ring[ip % kStatsRing]);
         } else {
-          request(ip - kItems, nbase, ring[ip % kStatsRing]);
+          request(ip - kItems, nbase, ring[ip % kStatsRing], base < last);
         }
         if (i == 0) {
 #pragma unroll
