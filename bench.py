@@ -68,9 +68,12 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the 10B-fragment line")
     ap.add_argument("--reported", action="store_true",
-                    help="time the reported, ungated sets (4096^2 cold, 24-fragment cycles of the 135M set "
-                         "and of the edge mix) and print them as one JSON line")
-    ap.add_argument("--reported-only", default=None, help="comma-separated subset of c1,c2,c5k1,c5k16")
+                    help="time the reported, ungated sets (4096^2 cold, the 10B set's largest fragment, "
+                         "24-fragment cycles of the 135M set and of the edge mix, the next rows' calls) "
+                         "and print them as one JSON line")
+    ap.add_argument("--reported-only", default=None,
+                    help="comma-separated subset of c1,c4_largest,c2,c5k1,c5k16,native_c2,native_c5k1,"
+                         "broadcast_c3,stale_c3,ring_study,ring_c3,rda_c3")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a device-to-device copy of known size (counter calibration)")
     return ap.parse_args()
@@ -86,15 +89,15 @@ def fragment_ids(cfg, which):
     return [t for t, f in enumerate(frag) if f == p], p
 
 
-def build_workload(key, device):
+def build_workload(key, device, which="median"):
     import workloads
     cfg = workloads.config(key)
     if cfg.n_fragments == 1:
         ids, frag = list(range(len(cfg.tensors))), 0
         desc = f"{cfg.title}; one outer step over all {len(ids)} tensors"
     else:
-        ids, frag = fragment_ids(cfg, "median")
-        desc = f"{cfg.title}; median fragment {frag} of {cfg.n_fragments} ({len(ids)} tensors)"
+        ids, frag = fragment_ids(cfg, which)
+        desc = f"{cfg.title}; {which} fragment {frag} of {cfg.n_fragments} ({len(ids)} tensors)"
     inp = workloads.fragment_inputs(cfg, ids, device, fragment=frag)
     return cfg, inp, desc
 
@@ -126,9 +129,9 @@ class Runner:
                                       self.inp.tensors, self.lr, self.beta)
 
 
-def time_workload(key, steps, warmup, device):
+def time_workload(key, steps, warmup, device, which="median"):
     import torch
-    cfg, inp, desc = build_workload(key, device)
+    cfg, inp, desc = build_workload(key, device, which)
     torch.cuda.synchronize()
     n_params = sum(n for _, _, n in inp.tensors)
     kp = sum(1 for p in inp.present if p)
@@ -543,14 +546,27 @@ def rda_rate(key, device, reps=5, warmup=2):
 
 def reported(device, only=None):
     """The parameter sets that are reported but not gated: the 4096^2 tensor (cold
-    cache), and full 24-fragment cycles of the 135M set and of the edge mix."""
+    cache), the 10B set's largest fragment, full 24-fragment cycles of the 135M set
+    and of the edge mix, and the calls of the next rows on the 1B set."""
     import torch
-    keys = only.split(",") if only else ["c1", "c2", "c5k1", "c5k16", "native_c2", "native_c5k1", "broadcast_c3",
+    keys = only.split(",") if only else ["c1", "c4_largest", "c2", "c5k1", "c5k16", "native_c2", "native_c5k1",
+                                         "broadcast_c3",
                                          "stale_c3", "ring_study", "ring_c3", "rda_c3"]
     out = {}
     if "c1" in keys:
         out["c1"] = single_call_cold("c1", device)
         print(f"# c1 {out['c1']['ms']:.3f} ms", file=sys.stderr, flush=True)
+    if "c4_largest" in keys:
+        # the 10B set's largest fragment: one tensor of 525,336,576 params, K = 14
+        res = time_workload("c4", 5, 2, device, which="largest")
+        out["c4_largest"] = {k: res[k] for k in ("desc", "n_params", "n_tensors", "k_present", "step_ms",
+                                                 "stage_ms", "params_per_s", "hbm_gbps", "stage_gbps",
+                                                 "bytes_per_param")}
+        out["c4_largest"]["hbm_frac"] = res["hbm_gbps"] / PEAK_HBM_GBPS
+        del res
+        torch.cuda.empty_cache()
+        print(f"# c4 largest fragment {out['c4_largest']['step_ms']:.3f} ms, "
+              f"{out['c4_largest']['hbm_gbps']:.0f} GB/s", file=sys.stderr, flush=True)
     for key in [k for k in keys if k.startswith("native_")]:
         out[key] = native_cycle(key[len("native_"):], device)
         torch.cuda.empty_cache()
