@@ -117,7 +117,8 @@ Partition stats_partition(const dlc_tensor* t, int32_t n) {
 }
 
 Partition encode_partition(const dlc_tensor* t, int32_t n) {
-  return make_partition(t, n, dlc::kMaxEncodeTiles, kEncodeBlocks, 1, kEncodeMinTiles);
+  // whole groups per block: the blocks of a tensor take its groups in turn
+  return make_partition(t, n, dlc::kMaxEncodeTiles, kEncodeBlocks, dlc::kEncodeGroupTiles, kEncodeMinTiles);
 }
 
 Partition broadcast_partition(const dlc_tensor* t, int32_t n) {

@@ -26,9 +26,11 @@ constexpr int kLearnerChunk = 16;         // learners per encode launch
 // Bucket histograms are packed 64-bit integers: bits 44..63 count elements, bits
 // 0..43 sum each element's position inside its bucket in units of wd * 2^-s
 // (s <= kHistFracBits), offset by kHistBias.  An encode block covers at most
-// kMaxEncodeTiles tiles of a tensor (2^17 elements per learner), so neither field
-// can overflow: 2^17 * 2^27 <= 2^44 and 2^17 < 2^20.
-constexpr int kMaxEncodeTiles = 32;
+// kMaxEncodeTiles full tiles of a tensor (whole groups of 4 tiles) plus, in the
+// tensor's last block, its partial last tile: under 29 * 4096 < 2^17 elements per
+// learner, so neither field can overflow: 2^17 * 2^27 <= 2^44 and 2^17 < 2^20.
+constexpr int kMaxEncodeTiles = 28;
+constexpr int kEncodeGroupTiles = 4;      // tiles per encode group
 // The codebook stage sums a tensor's block histograms in slices of kHistSlice
 // blocks (unpacked: 64 * 2^17 elements keep the count within 2^23 and the
 // position sum within 2^50), then the slices.

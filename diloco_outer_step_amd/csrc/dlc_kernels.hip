@@ -481,7 +481,9 @@ __device__ __forceinline__ void store_codes(uint8_t* cp, bool valid, int tid, co
   for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_buffer_store_b32(packed[j], r, f4_index(tid, j) * 4, 0, 2);
 }
 
-// Order of work.  A block's full tiles form groups of kGroup consecutive tiles.
+// Order of work.  A tensor's full tiles form groups of kGroup consecutive tiles,
+// dealt to the tensor's blocks in turn (block j of nb takes groups j, j + nb, ...),
+// so blocks that run at the same time stream neighbouring parts of every buffer.
 // For each group, theta_g's kGroup tiles are held in registers while every
 // learner is encoded against them, one learner at a time; a learner's codes of the
 // whole group (kGroup * 4 KB, contiguous) leave in one burst of stores once its
@@ -491,12 +493,13 @@ __device__ __forceinline__ void store_codes(uint8_t* cp, bool valid, int tid, co
 // items ahead is requested before a tile is encoded, across learner and group
 // boundaries.  theta_g's tile u of the next group is requested into its own
 // registers as soon as the group's last learner has encoded tile u.  A request for
-// a tile beyond the block's full tiles (a partial last group, or past the end) is a
-// null request: no memory traffic, and the tile is skipped.  Every load and store
+// a tile beyond the tensor's full tiles (a partial last group) or past the block's
+// last group is a null request: no memory traffic, and the tile is skipped.  The
+// tensor's partial last tile, if any, is encoded by its last block.  Every load and store
 // is unconditional, so the compiler's wait counts stay exact.
 // Per-learner {lo, hi, wd, 1/wd, fixed-point constants} are staged in LDS once
 // per block.
-constexpr int kGroup = 4;
+constexpr int kGroup = kEncodeGroupTiles;
 
 template <int R>
 __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const LaunchGeom g) {
@@ -506,35 +509,37 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
   EncodePar* par = reinterpret_cast<EncodePar*>(smem + kc * R * kHistBytes);
   const int tid = threadIdx.x;
 
+  // Block -> (tensor t, rank j among the tensor's nb blocks).  Block j encodes the
+  // tensor's groups j, j + nb, j + 2 nb, ...: blocks that run at the same time
+  // work on neighbouring groups.
   const Span sp = block_span(g);
-  const TensorDesc td = g.t[sp.t];
-  const size_t rrow = (size_t)g.row_base + g.t_base + sp.t;
+  const int t = sp.t;
+  const TensorDesc td = g.t[t];
+  const int j = blockIdx.x - td.block_first;
+  const int nb = tensor_block_end(g, t) - td.block_first;
+  const size_t rrow = (size_t)g.row_base + g.t_base + t;
   for (int i = tid; i < kc * R * kBuckets; i += kBlock) hist[i] = 0;
   if (tid < kc) par[tid] = make_encode_par(a.range[(size_t)a.learner[a.k_base + tid] * g.n_tensors_call + rrow]);
   __syncthreads();
 
   const bool has_base = a.theta_g != nullptr;  // NULL: Delta = fl32(0 - theta_L), base tiles are zeros
-  const float* __restrict__ tg = has_base ? a.theta_g + td.offset() + sp.begin : learner_row(a, 0, td) + sp.begin;
+  const float* __restrict__ tg = has_base ? a.theta_g + td.offset() : learner_row(a, 0, td);
   auto codes_of = [&](int k) {
-    return a.codes + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset() + sp.begin;
+    return a.codes + (int64_t)a.learner[a.k_base + k] * a.stride + td.loffset();
   };
 
-  const int64_t n_full = (sp.end - sp.begin) / kTile;
-  if (n_full > 0) {
-    const int64_t n_groups = (n_full + kGroup - 1) / kGroup;
-    // tile u of group grp of stream s (0 = theta_g, s >= 1 = learner s - 1)
-    auto request = [&](float (&dst)[kVec], int64_t grp, int s, int u) {
-      const int64_t tile = grp * kGroup + u;
-      const bool valid = tile < n_full && (s != 0 || has_base);
-      const float* base = s == 0 ? tg : learner_row(a, s - 1, td) + sp.begin;
+  const int64_t n_full = td.numel() / kTile;  // full tiles of the tensor
+  const int64_t groups_total = (n_full + kGroup - 1) / kGroup;
+  const int64_t n_groups = groups_total > j ? (groups_total - j + nb - 1) / nb : 0;  // this block's groups
+  if (n_groups > 0) {
+    // tile u of this block's group gi of stream s (0 = theta_g, s >= 1 = learner s - 1)
+    auto request = [&](float (&dst)[kVec], int64_t gi, int s, int u) {
+      const int64_t tile = (j + gi * nb) * kGroup + u;
+      const bool valid = gi < n_groups && tile < n_full && (s != 0 || has_base);
+      const float* base = s == 0 ? tg : learner_row(a, s - 1, td);
       load_tile_rsrc(tile_rsrc(base + (valid ? tile : 0) * kTile, valid), tid, dst);
     };
     float gv[kGroup][kVec], ring[kGroup][kVec];
-    // Prologue in the order a pass leaves its requests behind: theta_g's tiles,
-    // the first three learner tiles, then one pass worth of (null) code stores.
-    // Every way into the learner loop then carries the same sequence of memory
-    // operations, so the static wait counts at each tile's first use fit all of
-    // them without draining the ring.
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) request(gv[u], 0, 0, u);
 #pragma unroll
@@ -545,26 +550,25 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
       for (int u = 0; u < kGroup; ++u) store_codes(codes_of(0), false, tid, zero);
     }
     __builtin_amdgcn_sched_barrier(0);
-    for (int64_t grp = 0; grp < n_groups; ++grp) {
+    for (int64_t gi = 0; gi < n_groups; ++gi) {
+      const int64_t grp = j + gi * nb;
       const int64_t left = n_full - grp * kGroup;
       const int valid = left < kGroup ? (int)left : kGroup;
-      // learner k over the group; kLast: the group's last learner, whose look-ahead
-      // runs into the next group
       auto pass = [&](int k, auto last_tag) {
         constexpr bool kLast = decltype(last_tag)::value;
         uint32_t cw[kGroup][4];
 #pragma unroll
         for (int u = 0; u < kGroup; ++u) {
-          if (u == 0) request(ring[kGroup - 1], grp, k + 1, kGroup - 1);
-          else if (kLast) request(ring[u - 1], grp + 1, 1, u - 1);
-          else request(ring[u - 1], grp, k + 2, u - 1);
+          if (u == 0) request(ring[kGroup - 1], gi, k + 1, kGroup - 1);
+          else if (kLast) request(ring[u - 1], gi + 1, 1, u - 1);
+          else request(ring[u - 1], gi, k + 2, u - 1);
           if (u < valid) {
             encode_codes<true, R>(hist + k * R * kBuckets, gv[u], ring[u], par[k], tid, kTile, cw[u]);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) cw[u][j] = 0u;
+            for (int q = 0; q < 4; ++q) cw[u][q] = 0u;
           }
-          if (kLast) request(gv[u], grp + 1, 0, u);
+          if (kLast) request(gv[u], gi + 1, 0, u);
         }
         uint8_t* cp = codes_of(k) + grp * kGroup * kTile;
 #pragma unroll
@@ -574,22 +578,23 @@ __global__ __launch_bounds__(kBlock) void k_encode(const QuantArgs a, const Laun
       pass(kc - 1, std::true_type{});
     }
   }
+  // The partial last tile of the tensor, if any, belongs to the tensor's last block.
   const int64_t full_len = n_full * kTile;
-  if (sp.begin + full_len < sp.end) {
-    const int64_t n = sp.end - sp.begin - full_len;
+  if (j == nb - 1 && full_len < td.numel()) {
+    const int64_t n = td.numel() - full_len;
     float gv[kVec];
     load_tail(tg + full_len, tid, has_base ? n : 0, gv);
     for (int k = 0; k < kc; ++k) {
       float lv[kVec];
-      load_tail(learner_row(a, k, td) + sp.begin + full_len, tid, n, lv);
+      load_tail(learner_row(a, k, td) + full_len, tid, n, lv);
       uint32_t cw[4];
       encode_codes<false, R>(hist + k * R * kBuckets, gv, lv, par[k], tid, n, cw);
       uint8_t* cp = codes_of(k) + full_len;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int q = 0; q < 4; ++q) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          if (tail_valid(tid, j, c, n)) cp[elem_index(tid, j, c)] = (uint8_t)(cw[j] >> (8 * c));
+          if (tail_valid(tid, q, c, n)) cp[elem_index(tid, q, c)] = (uint8_t)(cw[q] >> (8 * c));
         }
       }
     }
