@@ -495,8 +495,8 @@ __device__ __forceinline__ void store_codes(uint8_t* cp, bool valid, int tid, co
 // registers as soon as the group's last learner has encoded tile u.  A request for
 // a tile beyond the tensor's full tiles (a partial last group) or past the block's
 // last group is a null request: no memory traffic, and the tile is skipped.  The
-// tensor's partial last tile, if any, is encoded by its last block.  Every load and store
-// is unconditional, so the compiler's wait counts stay exact.
+// tensor's partial last tile, if any, is encoded by its last block.  Every load
+// and store is unconditional, so the compiler's wait counts stay exact.
 // Per-learner {lo, hi, wd, 1/wd, fixed-point constants} are staged in LDS once
 // per block.
 constexpr int kGroup = kEncodeGroupTiles;
