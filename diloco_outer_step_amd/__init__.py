@@ -25,9 +25,11 @@ DLC_ERR_ALIGNMENT = -2
 DLC_ERR_NO_QUORUM = -3
 DLC_ERR_WORKSPACE = -4
 DLC_ERR_HIP = -5
+DLC_ERR_NON_FINITE = -6
 DLC_RANGE_GIVEN = 1
 DLC_BROADCAST = 2
 DLC_TWO_LANES = 4
+DLC_DEBUG_CHECKS = 8
 DLC_MAX_LEARNERS = 64
 DLC_MAX_LANES = 8
 DLC_N_BUCKETS = 256
@@ -192,11 +194,13 @@ def dlc_quantize_encode(theta_g, theta_L, tensors, range_in, codes, codebook, wo
 
 
 def dlc_quantize(theta_g, theta_L, tensors, codes, codebook, range_io, workspace, present=None,
-                 range_given=False, stream=None):
+                 range_given=False, stream=None, debug_checks=False):
+    """debug_checks: raise DlcError (code DLC_ERR_NON_FINITE) when a present learner's
+    pseudo-gradient holds NaN or Inf; the call then synchronizes the stream."""
     k = theta_L.shape[0]
     arr, n = _tensors(tensors)
     _buf, pres = _present(present, k)
-    flags = DLC_RANGE_GIVEN if range_given else 0
+    flags = (DLC_RANGE_GIVEN if range_given else 0) | (DLC_DEBUG_CHECKS if debug_checks else 0)
     _check(_lib.dlc_quantize(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, pres, arr, n,
                              _ptr(codes), _ptr(codebook), _ptr(range_io), flags, _ptr(workspace),
                              workspace.numel(), _stream(stream)))

@@ -136,7 +136,7 @@ Partition merge_partition(const dlc_tensor* t, int32_t n) {
 }
 
 struct WorkspaceLayout {
-  size_t stats = 0, hist = 0, hist_sum = 0, total = 0;
+  size_t stats = 0, hist = 0, hist_sum = 0, status = 0, total = 0;
 };
 
 size_t round256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -149,7 +149,8 @@ WorkspaceLayout workspace_layout(int64_t stats_slots, int64_t hist_slots, int32_
   w.hist = round256((size_t)stats_slots * (size_t)n_learners * sizeof(double) * 2);
   w.hist_sum = w.hist + round256((size_t)hist_slots * (size_t)n_learners * dlc::kBuckets * sizeof(uint64_t));
   const size_t entries = (size_t)(hist_slots / dlc::kHistSlice) + (size_t)n_tensors + 2;
-  w.total = w.hist_sum + round256(entries * (size_t)n_learners * dlc::kBuckets * 2 * sizeof(uint64_t));
+  w.status = w.hist_sum + round256(entries * (size_t)n_learners * dlc::kBuckets * 2 * sizeof(uint64_t));
+  w.total = w.status + 256;  // one status word (debug checks), padded
   return w;
 }
 
@@ -192,6 +193,7 @@ struct Common {
   Partition part_stats;   // statistics pass (range stage)
   Partition part_enc;     // encode pass: blocks capped at kMaxEncodeTiles tiles
   hipStream_t stream;
+  uint32_t* status;       // the workspace's status word (used only by debug checks)
 };
 
 // Shared checks and setup of the quantize stages.
@@ -231,6 +233,7 @@ int32_t setup_quant(Common& c, const float* theta_global, const float* theta_lea
   c.args.part_stats = reinterpret_cast<double2*>(ws + wl.stats);
   c.args.part_hist = reinterpret_cast<uint64_t*>(ws + wl.hist);
   c.args.hist_sum = reinterpret_cast<uint64_t*>(ws + wl.hist_sum);
+  c.status = reinterpret_cast<uint32_t*>(ws + wl.status);
   c.stream = static_cast<hipStream_t>(hip_stream);
   return DLC_OK;
 }
@@ -617,7 +620,10 @@ int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
                      const dlc_tensor* tensors, int32_t n_tensors, uint8_t* codes,
                      float* codebook, float* range, uint32_t flags, void* workspace,
                      size_t workspace_bytes, void* hip_stream) {
-  if ((flags & ~DLC_RANGE_GIVEN) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
+  if ((flags & ~(DLC_RANGE_GIVEN | DLC_DEBUG_CHECKS)) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
+  const bool checks = (flags & DLC_DEBUG_CHECKS) != 0;
+  if (checks && (flags & DLC_RANGE_GIVEN) != 0)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "DLC_DEBUG_CHECKS needs the statistics stage (not DLC_RANGE_GIVEN)");
   Common c;
   int32_t rc = setup_quant(c, theta_global, theta_learners, learner_stride, n_learners, present, tensors,
                            n_tensors, workspace, workspace_bytes, hip_stream);
@@ -628,12 +634,29 @@ int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
   c.args.range = reinterpret_cast<float4*>(range);
   c.args.codes = codes;
   c.args.codebook = codebook;
+  constexpr uint32_t kNone = 0xFFFFFFFFu;
+  if (checks) {
+    hipError_t e = dlc::launch_fill_u32(c.status, kNone, c.stream);
+    if (e != hipSuccess) return hip_fail(e, "status word");
+    c.args.status = c.status;
+  }
   if ((flags & DLC_RANGE_GIVEN) == 0) {
     rc = run_range(c);
     if (rc != DLC_OK) return rc;
   }
   rc = run_encode(c);
-  return rc == DLC_OK ? ok() : rc;
+  if (rc != DLC_OK) return rc;
+  if (checks) {
+    uint32_t first = kNone;
+    hipError_t e = hipMemcpyAsync(&first, c.status, sizeof(first), hipMemcpyDeviceToHost, c.stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c.stream);
+    if (e != hipSuccess) return hip_fail(e, "debug checks");
+    if (first != kNone)
+      return fail(DLC_ERR_NON_FINITE, "learner " + std::to_string(first / (uint32_t)n_tensors) + ", tensor " +
+                                          std::to_string(first % (uint32_t)n_tensors) +
+                                          ": the pseudo-gradient holds NaN or Inf (the lowest such pair)");
+  }
+  return ok();
 }
 
 int32_t dlc_quantize_bases(const float* const* bases, const float* theta_learners, int64_t learner_stride,

@@ -83,6 +83,8 @@ struct QuantArgs {
   uint64_t* hist_sum;       // [slice entry][n_present][256][2] {position sum, count}, see hist_entry
   double* norm2;            // optional [n_learners][n_tensors_call]: sum over the tensor of the
                             // dequantized values squared, sum_c count_c * codebook_c^2 (fp64)
+  uint32_t* status;         // optional: lowest learner * n_tensors_call + row whose statistics
+                            // are not finite (k_range), 0xFFFFFFFF when none
 };
 
 struct MergeArgs {
@@ -130,6 +132,8 @@ struct RingArgs {
 // Kernel launchers (dlc_kernels.hip).  Each returns hipSuccess or the launch error.
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 hipError_t launch_range(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
+// *p = v, one device word written by a kernel (capturable, unlike a memset).
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, hipStream_t s);
 hipError_t launch_encode(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);
 // histogram slices, then the codebook (one kernel when every tensor has one slice)
 hipError_t launch_codebook(const QuantArgs& a, const LaunchGeom& g, hipStream_t s);

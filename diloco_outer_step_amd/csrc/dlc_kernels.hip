@@ -302,6 +302,10 @@ __global__ __launch_bounds__(kRangeThreads) void k_range(const QuantArgs a, cons
   S1 = r1[0];
   S2 = r2[0];
   const int li = a.learner[k];
+  // A NaN or an infinity among the pseudo-gradients makes a sum non-finite (finite
+  // fp32 values cannot overflow an fp64 sum of squares of up to 2^32 terms).
+  if (a.status != nullptr && !(__builtin_isfinite(S1) && __builtin_isfinite(S2)))
+    atomicMin(a.status, (uint32_t)((size_t)li * g.n_tensors_call + g.row_base + g.t_base + t));
   const float g0 = a.theta_g != nullptr ? a.theta_g[td.offset()] : 0.0f;
   const float l0 = a.theta_L[(int64_t)li * a.stride + td.loffset()];
   const double shift = (double)(g0 - l0);
@@ -1197,6 +1201,12 @@ hipError_t allow_lds(K kernel, size_t lds) {
                              (int)lds);
 }
 
+// One device word, written by a kernel (a memset node may not replay correctly in a
+// captured graph).
+__global__ __launch_bounds__(64) void k_fill_u32(uint32_t* p, uint32_t v) {
+  if (threadIdx.x == 0) *p = v;
+}
+
 }  // namespace
 
 hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) {
@@ -1212,6 +1222,11 @@ hipError_t launch_stats(const QuantArgs& a, const LaunchGeom& g, hipStream_t s) 
   } else {
     hipLaunchKernelGGL(k_stats<14>, grid, block, 0, s, a, g);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t v, hipStream_t s) {
+  hipLaunchKernelGGL(k_fill_u32, dim3(1), dim3(64), 0, s, p, v);
   return hipGetLastError();
 }
 

@@ -26,7 +26,8 @@
  *     calling thread is returned by dlc_last_error().  No exception crosses the ABI.
  *   - Ownership: every buffer is owned by the caller.  The library allocates and
  *     frees no memory, keeps no state between calls and never synchronizes the
- *     stream.  Device pointers must be on the current HIP device.
+ *     stream (except dlc_quantize with DLC_DEBUG_CHECKS).  Device pointers must be
+ *     on the current HIP device.
  *   - Execution: work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
  *     stream).  Argument errors are returned before anything is enqueued; a failed
  *     launch returns DLC_ERR_HIP.  Two calls in flight at once must not share any
@@ -60,6 +61,7 @@ extern "C" {
 #define DLC_ERR_NO_QUORUM (-3)
 #define DLC_ERR_WORKSPACE (-4)
 #define DLC_ERR_HIP (-5)
+#define DLC_ERR_NON_FINITE (-6)
 
 /* dlc_quantize flag: use the caller's `range` instead of computing it. */
 #define DLC_RANGE_GIVEN 1u
@@ -71,6 +73,9 @@ extern "C" {
    lane's half of the workspace, so consecutive fragments overlap entirely.  Needs
    twice dlc_cycle_workspace_bytes. */
 #define DLC_TWO_LANES 4u
+/* dlc_quantize flag: also check that every present learner's pseudo-gradient is
+   finite (see dlc_quantize). */
+#define DLC_DEBUG_CHECKS 8u
 
 #define DLC_MAX_LEARNERS 64
 #define DLC_MAX_LANES 8
@@ -152,6 +157,14 @@ int32_t dlc_quantize_encode(const float* theta_global, const float* theta_learne
  * dlc_quantize -- dlc_quantize_range followed by dlc_quantize_encode.  With
  * DLC_RANGE_GIVEN in `flags`, `range` is an input (lo <= hi) and only the encode
  * stage runs.
+ * With DLC_DEBUG_CHECKS in `flags` (not together with DLC_RANGE_GIVEN), the
+ * statistics stage also records every (learner, tensor) whose pseudo-gradient
+ * holds a NaN or an infinity (NaN and Inf inputs are outside the contract: the
+ * kernels stay within their buffers, but codes, codebooks and ranges of such a
+ * tensor are meaningless).  The call then waits for `hip_stream` before it
+ * returns -- the one call mode that synchronizes, so it cannot be captured in a
+ * graph -- and returns DLC_ERR_NON_FINITE naming the lowest such (learner,
+ * tensor) pair; the outputs have been written all the same.
  */
 int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
                      int64_t learner_stride, int32_t n_learners, const uint8_t* present,

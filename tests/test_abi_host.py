@@ -42,7 +42,7 @@ def test_header_constants_match_binding():
     for name in ("DLC_OK", "DLC_ERR_INVALID_ARGUMENT", "DLC_ERR_ALIGNMENT", "DLC_ERR_NO_QUORUM",
                  "DLC_ERR_WORKSPACE", "DLC_ERR_HIP", "DLC_MAX_LEARNERS", "DLC_N_BUCKETS",
                  "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS", "DLC_RANGE_GIVEN", "DLC_BROADCAST", "DLC_TWO_LANES",
-                 "DLC_MAX_LANES"):
+                 "DLC_MAX_LANES", "DLC_ERR_NON_FINITE", "DLC_DEBUG_CHECKS"):
         m = re.search(rf"#define {name} \(?(-?\d+)u?\)?", text)
         assert m and int(m.group(1)) == getattr(dlc, name), name
 
@@ -233,7 +233,8 @@ def test_rda_and_ring_workspace_sizes():
     (lambda: quantize(present=[0, 0]), dlc.DLC_ERR_NO_QUORUM),
     (lambda: quantize(ws_bytes=16), dlc.DLC_ERR_WORKSPACE),
     (lambda: quantize(ws=None), dlc.DLC_ERR_WORKSPACE),
-    (lambda: quantize(flags=8), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(flags=16), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize(flags=dlc.DLC_DEBUG_CHECKS | dlc.DLC_RANGE_GIVEN), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: merge(weights=(0.0, 0.0)), dlc.DLC_ERR_NO_QUORUM),
     (lambda: merge(weights=(1.0, -1.0)), dlc.DLC_ERR_INVALID_ARGUMENT),
     (lambda: merge(weights=(1.0, float("nan"))), dlc.DLC_ERR_INVALID_ARGUMENT),
