@@ -17,7 +17,9 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdlc.so")
+# DLC_LIBRARY selects another build of the same library (the host-sanitized one
+# for host-only tests); the default is the in-tree libdlc.so.
+LIB_PATH = os.environ.get("DLC_LIBRARY") or os.path.join(_PKG, "libdlc.so")
 
 DLC_OK = 0
 DLC_ERR_INVALID_ARGUMENT = -1
@@ -123,6 +125,85 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+class _Checks:
+    """Refuse buffers the C ABI would reach out of bounds or misread: wrong type,
+    dtype, layout or size, then (after every other check, so that each of those
+    can be exercised on host tensors) a buffer not on the call's device."""
+
+    def __init__(self):
+        self.bufs = []
+
+    def need(self, t, name: str, dtype: torch.dtype, min_numel: int = 0):
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch.Tensor, not {type(t).__name__}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} must be {dtype}, not {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if t.numel() < min_numel:
+            raise ValueError(f"{name} holds {t.numel()} elements; the call needs at least {min_numel}")
+        self.bufs.append((name, t))
+
+    def learners(self, theta_L, tensors, name: str = "theta_L") -> Tuple[int, int]:
+        """(K, learner_stride) of a [K, learner_stride] fp32 tensor whose rows hold
+        every tensor's [loffset, loffset + numel)."""
+        if not isinstance(theta_L, torch.Tensor) or theta_L.dim() != 2:
+            raise ValueError(f"{name} must be a [K, learner_stride] tensor")
+        self.need(theta_L, name, torch.float32)
+        if _extents(tensors)[1] > theta_L.shape[1]:
+            raise ValueError(f"a tensor reaches past {name}'s row length {theta_L.shape[1]}")
+        return theta_L.shape[0], theta_L.shape[1]
+
+    def rows(self, t, name: str, k: int, stride: int, dtype: torch.dtype):
+        """A [k, stride] buffer mirroring the learner rows (codes, accumulators)."""
+        self.need(t, name, dtype)
+        if tuple(t.shape) != (k, stride):
+            raise ValueError(f"{name} must have shape ({k}, {stride}), not {tuple(t.shape)}")
+
+    def global_(self, tensors, **bufs):
+        """theta_global-shaped fp32 buffers cover every tensor's [offset, offset + numel)."""
+        end, _ = _extents(tensors)
+        for name, t in bufs.items():
+            self.need(t, name, torch.float32, end)
+
+    def outputs(self, k: int, rows: int, codes=None, stride=None, codebook=None, rng=None, sq_norms=None):
+        if codes is not None:
+            self.rows(codes, "codes", k, stride, torch.uint8)
+        if codebook is not None:
+            self.need(codebook, "codebook", torch.float32, k * rows * DLC_N_BUCKETS)
+        if rng is not None:
+            self.need(rng, "range", torch.float32, k * rows * DLC_RANGE_FIELDS)
+        if sq_norms is not None:
+            self.need(sq_norms, "sq_norms", torch.float64, k * rows)
+
+    def workspace(self, ws):
+        self.need(ws, "workspace", torch.uint8)
+
+    def done(self):
+        """Every buffer on one device, and that device a GPU."""
+        dev = None
+        for name, t in self.bufs:
+            if not t.is_cuda:
+                raise ValueError(f"{name} must be a device tensor, not on {t.device}")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name} is on {t.device}, the call's other buffers on {dev}")
+
+
+def _extents(tensors) -> Tuple[int, int]:
+    """(end of the last tensor in theta_global, end of the last in a learner row)."""
+    if len(tensors) == 0:
+        return 0, 0
+    return max(int(o) + int(n) for o, _, n in tensors), max(int(lo) + int(n) for _, lo, n in tensors)
+
+
+def _weights(weights, k: int, name: str = "weights"):
+    if len(weights) != k:
+        raise ValueError(f"{name} holds {len(weights)} values for {k} learners")
+    return (ctypes.c_double * k)(*[float(x) for x in weights])
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -138,10 +219,9 @@ def _present(present, k):
     return buf, ctypes.cast(buf, ctypes.c_void_p)
 
 
-def _learner_stride(theta_L: torch.Tensor) -> int:
-    if theta_L.dim() != 2 or not theta_L.is_contiguous():
-        raise ValueError("theta_L must be a contiguous [K, learner_stride] tensor")
-    return theta_L.shape[1]
+def _present_list(present, k):
+    if present is not None and len(present) != k:
+        raise ValueError(f"present holds {len(present)} values for {k} learners")
 
 
 def dlc_version() -> str:
@@ -176,19 +256,31 @@ def alloc_workspace(n_learners: int, tensors, device="cuda") -> torch.Tensor:
 
 
 def dlc_quantize_range(theta_g, theta_L, tensors, range_out, workspace, present=None, stream=None):
-    k = theta_L.shape[0]
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
+    _present_list(present, k)
+    c.global_(tensors, theta_g=theta_g)
+    c.outputs(k, len(tensors), rng=range_out)
+    c.workspace(workspace)
+    c.done()
     arr, n = _tensors(tensors)
     _buf, pres = _present(present, k)
-    _check(_lib.dlc_quantize_range(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, pres, arr, n,
+    _check(_lib.dlc_quantize_range(_ptr(theta_g), _ptr(theta_L), stride, k, pres, arr, n,
                                    _ptr(range_out), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 def dlc_quantize_encode(theta_g, theta_L, tensors, range_in, codes, codebook, workspace, present=None,
                         stream=None):
-    k = theta_L.shape[0]
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
+    _present_list(present, k)
+    c.global_(tensors, theta_g=theta_g)
+    c.outputs(k, len(tensors), codes, stride, codebook, range_in)
+    c.workspace(workspace)
+    c.done()
     arr, n = _tensors(tensors)
     _buf, pres = _present(present, k)
-    _check(_lib.dlc_quantize_encode(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, pres, arr, n,
+    _check(_lib.dlc_quantize_encode(_ptr(theta_g), _ptr(theta_L), stride, k, pres, arr, n,
                                     _ptr(range_in), _ptr(codes), _ptr(codebook), _ptr(workspace),
                                     workspace.numel(), _stream(stream)))
 
@@ -197,21 +289,34 @@ def dlc_quantize(theta_g, theta_L, tensors, codes, codebook, range_io, workspace
                  range_given=False, stream=None, debug_checks=False):
     """debug_checks: raise DlcError (code DLC_ERR_NON_FINITE) when a present learner's
     pseudo-gradient holds NaN or Inf; the call then synchronizes the stream."""
-    k = theta_L.shape[0]
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
+    _present_list(present, k)
+    c.global_(tensors, theta_g=theta_g)
+    c.outputs(k, len(tensors), codes, stride, codebook, range_io)
+    c.workspace(workspace)
+    c.done()
     arr, n = _tensors(tensors)
     _buf, pres = _present(present, k)
     flags = (DLC_RANGE_GIVEN if range_given else 0) | (DLC_DEBUG_CHECKS if debug_checks else 0)
-    _check(_lib.dlc_quantize(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, pres, arr, n,
+    _check(_lib.dlc_quantize(_ptr(theta_g), _ptr(theta_L), stride, k, pres, arr, n,
                              _ptr(codes), _ptr(codebook), _ptr(range_io), flags, _ptr(workspace),
                              workspace.numel(), _stream(stream)))
 
 
 def dlc_merge_outer_step(theta_g, momentum, codes, codebook, weights, tensors, lr=0.7, beta=0.9,
                          stream=None):
-    k = codes.shape[0]
-    if codes.dim() != 2 or not codes.is_contiguous():
-        raise ValueError("codes must be a contiguous [K, learner_stride] uint8 tensor")
-    w = (ctypes.c_double * k)(*[float(x) for x in weights])
+    if not isinstance(codes, torch.Tensor) or codes.dim() != 2:
+        raise ValueError("codes must be a [K, learner_stride] uint8 tensor")
+    k, stride = codes.shape
+    w = _weights(weights, k)
+    c = _Checks()
+    c.rows(codes, "codes", k, stride, torch.uint8)
+    c.global_(tensors, theta_g=theta_g, momentum=momentum)
+    if _extents(tensors)[1] > stride:
+        raise ValueError(f"a tensor reaches past learner_stride {stride}")
+    c.outputs(k, len(tensors), codebook=codebook)
+    c.done()
     arr, n = _tensors(tensors)
     _check(_lib.dlc_merge_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(codes), codes.shape[1], k,
                                      _ptr(codebook), ctypes.cast(w, ctypes.c_void_p), arr, n, float(lr),
@@ -222,13 +327,19 @@ def dlc_quantize_bases(bases, theta_L, tensors, codes, codebook, range_out, work
                        stream=None):
     """dlc_quantize with learner i's pseudo-gradient taken against bases[i] (a
     device tensor laid out like theta_g)."""
-    k = theta_L.shape[0]
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
     if len(bases) != k:
         raise ValueError("one base per learner")
+    _present_list(present, k)
+    c.global_(tensors, **{f"bases[{i}]": b for i, b in enumerate(bases) if present is None or present[i]})
+    c.outputs(k, len(tensors), codes, stride, codebook, range_out)
+    c.workspace(workspace)
+    c.done()
     arr, n = _tensors(tensors)
     _buf, pres = _present(present, k)
     ptrs = (ctypes.c_void_p * k)(*[b.data_ptr() for b in bases])
-    _check(_lib.dlc_quantize_bases(ctypes.cast(ptrs, ctypes.c_void_p), _ptr(theta_L), _learner_stride(theta_L), k,
+    _check(_lib.dlc_quantize_bases(ctypes.cast(ptrs, ctypes.c_void_p), _ptr(theta_L), stride, k,
                                    pres, arr, n, _ptr(codes), _ptr(codebook), _ptr(range_out), _ptr(workspace),
                                    workspace.numel(), _stream(stream)))
 
@@ -236,6 +347,8 @@ def dlc_quantize_bases(bases, theta_L, tensors, codes, codebook, range_out, work
 def dlc_merge_weights(tokens, arrival, quorum: int, grace: float):
     """-> (weights list, merge_time); raises NoQuorumError when the quorum is not met."""
     k = len(tokens)
+    if len(arrival) != k:
+        raise ValueError(f"arrival holds {len(arrival)} values for {k} learners")
     t = (ctypes.c_double * k)(*[float(x) for x in tokens])
     a = (ctypes.c_double * k)(*[float(x) for x in arrival])
     w = (ctypes.c_double * k)()
@@ -266,9 +379,15 @@ def ring_buffers(theta_L, n_tensors: int):
 
 def dlc_ring_outer_step(theta_g, momentum, theta_L, tensors, accum, codes, codebook, range_out, workspace, lr=0.7,
                         beta=0.9, stream=None):
-    k = theta_L.shape[0]
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
+    c.global_(tensors, theta_g=theta_g, momentum=momentum)
+    c.rows(accum, "accum", k, stride, torch.float32)
+    c.outputs(k, len(tensors), codes, stride, codebook, range_out)
+    c.workspace(workspace)
+    c.done()
     arr, n = _tensors(tensors)
-    _check(_lib.dlc_ring_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k, arr, n,
+    _check(_lib.dlc_ring_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), stride, k, arr, n,
                                     float(lr), float(beta), _ptr(accum), _ptr(codes), _ptr(codebook), _ptr(range_out),
                                     _ptr(workspace), workspace.numel(), _stream(stream)))
 
@@ -284,12 +403,15 @@ def dlc_rda_outer_step(theta_g, momentum, theta_L, tensors, weights, codes, code
                        lr=0.7, beta=0.9, stream=None):
     """One outer step merged by Radial-Directional Averaging; sq_norms is a device
     fp64 [K, n_tensors] output (squared norms of the dequantized pseudo-gradients)."""
-    k = theta_L.shape[0]
-    if sq_norms.dtype != torch.float64:
-        raise ValueError("sq_norms must be float64")
-    w = (ctypes.c_double * k)(*[float(x) for x in weights])
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
+    w = _weights(weights, k)
+    c.global_(tensors, theta_g=theta_g, momentum=momentum)
+    c.outputs(k, len(tensors), codes, stride, codebook, range_out, sq_norms)
+    c.workspace(workspace)
+    c.done()
     arr, n = _tensors(tensors)
-    _check(_lib.dlc_rda_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k, arr, n,
+    _check(_lib.dlc_rda_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), stride, k, arr, n,
                                    ctypes.cast(w, ctypes.c_void_p), float(lr), float(beta), _ptr(codes),
                                    _ptr(codebook), _ptr(range_out), _ptr(sq_norms), _ptr(workspace),
                                    workspace.numel(), _stream(stream)))
@@ -298,10 +420,15 @@ def dlc_rda_outer_step(theta_g, momentum, theta_L, tensors, weights, codes, code
 def dlc_broadcast(theta_g, theta_L, tensors, rows=None, stream=None):
     """Copy each tensor's theta_g into the learner rows of theta_L (all rows, or
     those with rows[i] true)."""
-    k = theta_L.shape[0]
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
+    if rows is not None and len(rows) != k:
+        raise ValueError(f"rows holds {len(rows)} values for {k} learners")
+    c.global_(tensors, theta_g=theta_g)
+    c.done()
     arr, n = _tensors(tensors)
     _buf, sel = _present(rows, k)
-    _check(_lib.dlc_broadcast(_ptr(theta_g), _ptr(theta_L), _learner_stride(theta_L), k, sel, arr, n,
+    _check(_lib.dlc_broadcast(_ptr(theta_g), _ptr(theta_L), stride, k, sel, arr, n,
                               _stream(stream)))
 
 
@@ -322,6 +449,22 @@ def group_by_fragment(tensors, fragment_of, n_fragments):
     return [tensors[t] for t in order], first, order
 
 
+def _cycle_checks(theta_g, momentum, theta_L, tensors, nf, weights, codes, codebook, range_out, workspace):
+    """Buffer checks of a fragment cycle -> (weights as a C array, K, learner_stride)."""
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
+    if len(weights) != nf:
+        raise ValueError(f"weights holds {len(weights)} rows for {nf} fragments")
+    for f, row in enumerate(weights):
+        if len(row) != k:
+            raise ValueError(f"weights[{f}] holds {len(row)} values for {k} learners")
+    c.global_(tensors, theta_g=theta_g, momentum=momentum)
+    c.outputs(k, len(tensors), codes, stride, codebook, range_out)
+    c.workspace(workspace)
+    c.done()
+    return (ctypes.c_double * (nf * k))(*[float(x) for row in weights for x in row]), k, stride
+
+
 def dlc_cycle_workspace_bytes(n_learners: int, tensors, fragment_first) -> int:
     arr, _ = _tensors(tensors)
     _fb, fp = _fragments(fragment_first)
@@ -336,14 +479,13 @@ def dlc_outer_cycle(theta_g, momentum, theta_L, tensors, fragment_first, weights
     """One outer step over every fragment; weights is [n_fragments][n_learners].
     two_lanes: fragments alternate between the two streams (workspace of twice
     dlc_cycle_workspace_bytes)."""
-    k = theta_L.shape[0]
     nf = len(fragment_first) - 1
+    w, k, stride = _cycle_checks(theta_g, momentum, theta_L, tensors, nf, weights, codes, codebook, range_out, workspace)
     arr, _ = _tensors(tensors)
     _fb, fp = _fragments(fragment_first)
-    w = (ctypes.c_double * (nf * k))(*[float(x) for row in weights for x in row])
     qs = _stream(quantize_stream)
     ms = qs if merge_stream is None else _stream(merge_stream)
-    _check(_lib.dlc_outer_cycle(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k,
+    _check(_lib.dlc_outer_cycle(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), stride, k,
                                 ctypes.cast(w, ctypes.c_void_p), arr, fp, nf, _ptr(codes), _ptr(codebook),
                                 _ptr(range_out), float(lr), float(beta),
                                 (DLC_BROADCAST if broadcast else 0) | (DLC_TWO_LANES if two_lanes else 0),
@@ -354,13 +496,12 @@ def dlc_outer_cycle_lanes(theta_g, momentum, theta_L, tensors, fragment_first, w
                           workspace, streams, lr=0.7, beta=0.9, broadcast=False):
     """The fragment cycle with the non-empty fragments taking the given streams in
     turn (workspace of len(streams) times dlc_cycle_workspace_bytes)."""
-    k = theta_L.shape[0]
     nf = len(fragment_first) - 1
+    w, k, stride = _cycle_checks(theta_g, momentum, theta_L, tensors, nf, weights, codes, codebook, range_out, workspace)
     arr, _ = _tensors(tensors)
     _fb, fp = _fragments(fragment_first)
-    w = (ctypes.c_double * (nf * k))(*[float(x) for row in weights for x in row])
     ss = (ctypes.c_void_p * max(1, len(streams)))(*[_stream(s).value for s in streams])
-    _check(_lib.dlc_outer_cycle_lanes(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), _learner_stride(theta_L), k,
+    _check(_lib.dlc_outer_cycle_lanes(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), stride, k,
                                       ctypes.cast(w, ctypes.c_void_p), arr, fp, nf, _ptr(codes), _ptr(codebook),
                                       _ptr(range_out), float(lr), float(beta), DLC_BROADCAST if broadcast else 0,
                                       _ptr(workspace), workspace.numel(), ctypes.cast(ss, ctypes.c_void_p),

@@ -25,7 +25,8 @@ constexpr int kTile = kBlock * kVec;      // elements per tile
 constexpr int kLearnerChunk = 16;         // learners per encode launch
 // Bucket histograms are packed 64-bit integers: bits 44..63 count elements, bits
 // 0..43 sum each element's position inside its bucket in units of wd * 2^-s
-// (s <= kHistFracBits), offset by kHistBias.  An encode block covers at most
+// (s <= kHistFracBits), offset by a per-(learner, tensor) bias of at least kHistBias
+// that keeps every position in [0, 2^27).  An encode block covers at most
 // kMaxEncodeTiles full tiles of a tensor (whole groups of 4 tiles) plus, in the
 // tensor's last block, its partial last tile: under 29 * 4096 < 2^17 elements per
 // learner, so neither field can overflow: 2^17 * 2^27 <= 2^44 and 2^17 < 2^20.

@@ -354,32 +354,51 @@ __device__ __forceinline__ double uniform_f64(double v) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
-// Fraction bits s of the packed bucket-position sums for one (learner, tensor).
-// An element of bucket c contributes q = round((x_c - lo) * 2^s / wd) - c * 2^s
-// (plus a constant, see EncodePar).  For buckets 0..254, q lies within
-// [-2^12, 2^s + 2^12] (the fp32 bucket index can misplace x by at most
-// 3 * 2^-24 * 257 bucket widths); bucket 255 also holds the values up to hi, i.e.
-// q <= ((hi - lo) / wd - 255) * 2^s.  s is the largest value <= kHistFracBits that
-// keeps q + kHistBias below 2^27 (normally 26).
-__device__ __forceinline__ int hist_frac_bits(float lo, float hi, float wd) {
+// Fraction bits s and bias of the packed bucket-position sums for one (learner,
+// tensor).  An element of bucket c contributes its position inside the bucket,
+// q = round((x_c - lo) * 2^s / wd) - c * 2^s, plus the bias (see EncodePar).  In
+// bucket widths, with e = (hi - lo) / wd - 255:
+//   * an element in [lo, hi] that the fp32 index puts in bucket c < 255 sits in
+//     [-2^-14, 1 + 2^-14] (the index misplaces x by at most 3 * 2^-24 * 257 widths);
+//   * bucket 255 also holds the values clipped to hi: up to max(1, e);
+//   * an element above hi is clipped to hi but coded from its own value, so it can
+//     land in any bucket from floor((hi - lo) / wd) to 255.  Normally (hi - lo) / wd
+//     is about 256 and that is bucket 255 at a position >= 0; but when lo and hi
+//     round to fp32 steps coarser than wd (|mu| many orders above sigma, up to
+//     lo == hi) it is a bucket above hi's, at a position down to e < 0.
+// So q lies in [min(0, e) * 2^s - 2^12, max(1, e) * 2^s + 2^12] (plus 1 for the
+// roundings).  The bias lifts the lowest position to >= 0:
+//   bias = kHistBias + ceil(max(0, -e) * 2^s)
+// and s is the largest value <= kHistFracBits that keeps the highest, q + bias,
+// below 2^27: (max(1, e) + max(0, -e)) * 2^s + 2 * kHistBias < 2^27 (normally 26).
+struct HistFormat {
+  int s;
+  double bias;  // an integer
+};
+
+__device__ __forceinline__ HistFormat hist_format(float lo, float hi, float wd) {
   const double ext = ((double)hi - (double)lo) / (double)wd - 255.0;
   const double top = ext > 1.0 ? ext : 1.0;
+  const double neg = ext < 0.0 ? -ext : 0.0;
   int s = kHistFracBits;
-  while (s > 0 && top * (double)(1ll << s) + 2.0 * kHistBias >= (double)(1ll << 27)) --s;
-  return s;
+  while (s > 0 && (top + neg) * (double)(1ll << s) + 2.0 * kHistBias >= (double)(1ll << 27)) --s;
+  HistFormat f;
+  f.s = s;
+  f.bias = (double)kHistBias + __builtin_ceil(neg * (double)(1ll << s));
+  return f;
 }
 
 // Fixed-point bucket positions without integer conversions.  With scale = 2^s / wd,
 // B = -lo * scale and B_i = rint(B), the element's addend is the bit pattern of
-//   y = fl64(fl64(x_c * scale + (2^52 + 2^44 + B_i + kHistBias)) - c * 2^s)
+//   y = fl64(fl64(x_c * scale + (2^52 + 2^44 + B_i + bias)) - c * 2^s)
 // The first fused multiply-add rounds to an integer (the spacing of doubles in
 // [2^52, 2^53) is 1), so y = 2^52 + 2^44 + v with v = rint(x_c * scale) + B_i -
-// c * 2^s + kHistBias in [0, 2^27); the second is exact.  Its bits are
+// c * 2^s + bias in [0, 2^27) (HistFormat); the second is exact.  Its bits are
 // kPosUnit * 2^44 + v: the low 44 bits carry v, the top 20 bits the odd constant
 // kPosUnit, so a sum of N addends holds N * kPosUnit mod 2^20 on top (N < 2^20
 // per block, recovered with the inverse kPosUnitInv) and the sum of v below.
-// The exact position (x_c - lo) * scale - c * 2^s is v - kHistBias + (B - B_i)
-// within 1/2: the codebook adds the constant B - B_i back.
+// The exact position (x_c - lo) * scale - c * 2^s is v - bias + (B - B_i)
+// within 1/2: the codebook subtracts the bias and adds the constant B - B_i back.
 constexpr double kPosMagic = 0x1p52 + 0x1p44;
 constexpr uint64_t kPosUnit = 0x43301;  // top 20 bits of every addend
 constexpr uint64_t kPosUnitInv = 0x4cd01;  // kPosUnit * kPosUnitInv = 1 mod 2^20
@@ -390,9 +409,10 @@ static_assert(kHistCountShift == 44, "addend layout");
 struct EncodePar {
   float lo, hi, wd, rcp;  // clip range, bucket width, fl32(1 / wd)
   double scale;           // 2^s / wd
-  double magic;           // 2^52 + 2^44 + rint(-lo * scale) + kHistBias
+  double magic;           // 2^52 + 2^44 + rint(-lo * scale) + bias
   double neg_two_s;       // -2^s
   double origin_frac;     // -lo * scale - rint(-lo * scale)
+  double bias;            // HistFormat::bias
 };
 
 __device__ __forceinline__ EncodePar make_encode_par(float4 r) {
@@ -401,17 +421,18 @@ __device__ __forceinline__ EncodePar make_encode_par(float4 r) {
   p.hi = r.y;
   p.wd = r.z;
   p.rcp = 0.0f;
-  p.scale = p.magic = p.neg_two_s = p.origin_frac = 0.0;
+  p.scale = p.magic = p.neg_two_s = p.origin_frac = p.bias = 0.0;
   if (r.z >= FLT_MIN) {
     p.rcp = 1.0f / r.z;
-    const int s = hist_frac_bits(r.x, r.y, r.z);
-    const double two_s = (double)(1ll << s);
+    const HistFormat f = hist_format(r.x, r.y, r.z);
+    const double two_s = (double)(1ll << f.s);
     p.scale = two_s / (double)r.z;
     const double b = -(double)r.x * p.scale;
     const double bi = __builtin_rint(b);
-    p.magic = kPosMagic + (bi + (double)kHistBias);
+    p.magic = kPosMagic + (bi + f.bias);
     p.neg_two_s = -two_s;
     p.origin_frac = b - bi;
+    p.bias = f.bias;
   }
   return p;
 }
@@ -655,8 +676,8 @@ __device__ __forceinline__ double write_codebook(const QuantArgs& a, const Launc
     out = r.w;
     N = c == 0 ? (uint64_t)g.t[t].numel() : 0;
   } else if (N > 0) {
-    const int64_t Q = (int64_t)(Qb - N * (uint64_t)kHistBias);
     const EncodePar par = make_encode_par(r);
+    const int64_t Q = (int64_t)(Qb - N * (uint64_t)par.bias);
     const double frac = ((double)Q / (double)N + par.origin_frac) / -par.neg_two_s;
     out = (float)((double)r.x + (double)r.z * ((double)c + frac));
   } else {

@@ -7,7 +7,7 @@ import torch
 import diloco_outer_step_amd as dlc
 import oracle
 import workloads
-from tests import parity
+from tests import edge_inputs, parity
 
 pytestmark = pytest.mark.gpu
 
@@ -76,11 +76,32 @@ def case_inputs(name):
         for i, sigma in enumerate([3e-8, 2e-8, 1e-7]):
             theta_L[i] = theta - (1.0 + torch.randn(stride, generator=gen, device=DEV) * sigma)
         return workloads.StepInputs(theta, mom, theta_L, tensors, [1.0, 2.0, 1.0], [1, 1, 1], [0, 1, 2], stride)
+    if name == "above_hi_mean_dominated_k2":
+        return above_hi_inputs()
     raise KeyError(name)
 
 
+def above_hi_inputs():
+    """Learner 0: tensors whose (hi - lo) / wd is far from 256 (lo == hi, ~195, ~241,
+    ~248, ~271) with elements above hi, which the encode codes from their own
+    value but clips to hi; learner 1: ordinary Gaussian tensors with outliers.
+    theta_g = 0, so Delta = fl32(0 - theta_i) = -theta_i exactly."""
+    xs = [edge_inputs.case_input(name, args) for name, args, _ in edge_inputs.CASES]
+    tensors, stride = [], 0
+    for x in xs:
+        tensors.append((stride, stride, x.size))
+        stride += (x.size + 63) // 64 * 64
+    tl = np.zeros((2, stride), np.float32)
+    for t, (x, (_, lo, n)) in enumerate(zip(xs, tensors)):
+        tl[0, lo:lo + n] = -x
+        tl[1, lo:lo + n] = -edge_inputs.ordinary(100 + t, n)
+    theta = torch.zeros(stride, device=DEV)
+    return workloads.StepInputs(theta, torch.zeros(stride, device=DEV), torch.from_numpy(tl).to(DEV), tensors,
+                                [1.0, 2.0], [1, 1], list(range(len(xs))), stride)
+
+
 CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const", "sparse_k8",
-         "max_learners_k64", "mean_dominated_k3"]
+         "max_learners_k64", "mean_dominated_k3", "above_hi_mean_dominated_k2"]
 
 
 @pytest.mark.parametrize("name", CASES)

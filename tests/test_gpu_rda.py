@@ -21,6 +21,7 @@ import diloco_outer_step_amd as dlc
 import oracle
 import workloads
 from tests import parity
+from tests.test_gpu_parity import case_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -187,3 +188,23 @@ def test_rda_full_1b_set_sampled_tensors():
         assert parity.ulp_distance(parity.host(gpu["theta"][off:off + n]), th_o).max() <= 1
         assert parity.ulp_distance(parity.host(gpu["momentum"][off:off + n]), mo_o).max() <= 1
         print(f"[rda c3] tensor {t} ({n} params, K = {k}) ok", flush=True)
+
+
+@pytest.mark.parametrize("name", ["mean_dominated_k3", "above_hi_mean_dominated_k2"])
+def test_rda_norms_from_exact_bucket_counts(name):
+    """Pseudo-gradients whose mean dwarfs their spread, some with elements above hi:
+    the squared norms come from the bucket counts, so they equal sum_c n_c cb_c^2
+    with the oracle's counts n_c (codes identical end to end) and the GPU's entries;
+    then the oracle's RDA merge on the GPU's codes gives theta and momentum."""
+    inp = case_inputs(name)
+    gpu = gpu_rda(inp)
+    theta0, mom0 = parity.host(inp.theta_g), parity.host(inp.momentum)
+    orc = oracle.outer_step(theta0, mom0, parity.host(inp.theta_L), inp.theta_L.shape[1], inp.tensors, inp.weights,
+                            inp.present, LR, BETA, rule="rda")
+    rep = parity.compare(gpu, orc, inp, pinned=False, state=False)
+    assert rep["flips"] == 0
+    cb, norms = parity.host(gpu["codebook"]), parity.host(gpu["sq_norms"])
+    for (i, t), q in orc["quant"].items():
+        want = float(np.sum(q["bucket_count"] * cb[i, t].astype(np.float64) ** 2))
+        assert abs(norms[i, t] - want) <= 1e-12 * want, (i, t, norms[i, t], want)
+    check_merge_on_gpu_codes(gpu, inp, theta0, mom0)
