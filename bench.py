@@ -694,7 +694,16 @@ def _pool_merge(unit):
     return 0
 
 
-def cpu_baseline_parallel(res, budget_params=48_000_000, max_workers=16, check=False):
+def pool_workers():
+    """Worker processes for the oracle's pool: every core of this process's affinity
+    mask, within the host's CPU share for this job where the environment states
+    one (OMP_NUM_THREADS; 16 per GPU on the GPU hosts)."""
+    cores = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS", "")
+    return max(1, min(cores, int(share))) if share.isdigit() and int(share) > 0 else cores
+
+
+def cpu_baseline_parallel(res, budget_params=48_000_000, max_workers=None, check=False):
     """The oracle's functions over a process pool, on host copies of mid-size
     tensors of the same workload (each at most a quarter of the sample, so the
     units balance).  check=True also returns the pool's theta and momentum with
@@ -715,7 +724,7 @@ def cpu_baseline_parallel(res, budget_params=48_000_000, max_workers=16, check=F
     if not chosen:
         return None
     stride = sum((inp.tensors[t][2] + 63) // 64 * 64 for t in chosen)
-    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    workers = pool_workers() if max_workers is None else max(1, min(max_workers, pool_workers()))
     with tempfile.TemporaryDirectory() as tmp:
         spec = {"th": ([stride], "float32"), "mo": ([stride], "float32"), "tl": ([k, stride], "float32"),
                 "codes": ([k, stride], "uint8"), "cb": ([k, len(chosen), 256], "float32"),
@@ -755,17 +764,35 @@ def cpu_baseline_parallel(res, budget_params=48_000_000, max_workers=16, check=F
                 sample=f"{len(chosen)} mid-size tensors of the workload ({total} params, K={kp}): "
                        f"oracle.quantize_tensor per (tensor, learner), then oracle.merge + oracle.nesterov "
                        f"per tensor, on a pool of {workers} spawned processes; {dt:.2f} s",
-                seconds=dt)
+                seconds=dt, affinity_cores=len(os.sched_getaffinity(0)),
+                omp_num_threads=os.environ.get("OMP_NUM_THREADS"))
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it: model name, family/model/stepping,
+    physical cores and logical CPUs, and the cores this process may run on."""
+    info = {}
     try:
+        physical = set()
+        phys_id = None
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            key, _, val = line.partition(":")
+            key, val = key.strip(), val.strip()
+            if key == "physical id":
+                phys_id = val
+            elif key == "core id":
+                physical.add((phys_id, val))
+            elif key in ("model name", "cpu family", "model", "stepping") and key not in info:
+                info[key] = val
+        if physical:
+            info["physical_cores"] = len(physical)
     except OSError:
-        pass
-    return platform.processor()
+        info["model name"] = platform.processor()
+    info["logical_cpus"] = os.cpu_count()
+    info["affinity_cores"] = len(os.sched_getaffinity(0))
+    return (f"{info.get('model name', '?')} (family {info.get('cpu family', '?')}, model {info.get('model', '?')}, "
+            f"stepping {info.get('stepping', '?')}; {info.get('physical_cores', '?')} cores, "
+            f"{info['logical_cpus']} logical CPUs, {info['affinity_cores']} in this process's affinity mask)")
 
 
 def main():
@@ -810,7 +837,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": res["desc"], "params_per_step": res["n_params"], "tensors": res["n_tensors"],
                    "learners_present": res["k_present"], "lr": res["cfg"].lr, "momentum": res["cfg"].beta,
-                   "accumulation": "fp64 statistics, histogram sums and merge"},
+                   "accumulation": "fp64 statistics and merge; bucket sums as fixed-point integers"},
         "hbm_gbps": res["hbm_gbps"],
         "hbm_frac": res["hbm_gbps"] / PEAK_HBM_GBPS,
         "bytes_per_param": res["bytes_per_param"],
