@@ -37,10 +37,11 @@ DLC_MAX_LANES = 8
 DLC_N_BUCKETS = 256
 DLC_ALIGN_ELEMS = 64
 DLC_RANGE_FIELDS = 4
+DLC_STATIC_SCRATCH_BYTES = 64 << 20
 
 EXPORTED = (
     "dlc_fragment_plan", "dlc_workspace_bytes", "dlc_quantize_range", "dlc_quantize_encode",
-    "dlc_quantize", "dlc_quantize_bases", "dlc_merge_outer_step", "dlc_merge_weights", "dlc_broadcast",
+    "dlc_quantize", "dlc_quantize_static", "dlc_quantize_bases", "dlc_merge_outer_step", "dlc_merge_weights", "dlc_broadcast",
     "dlc_cycle_workspace_bytes", "dlc_outer_cycle", "dlc_outer_cycle_lanes", "dlc_ring_workspace_bytes", "dlc_ring_outer_step",
     "dlc_rda_workspace_bytes", "dlc_rda_outer_step", "dlc_last_error", "dlc_version",
 )
@@ -72,6 +73,7 @@ def _load() -> ctypes.CDLL:
         "dlc_quantize_range": [vp, vp, i64, i32, vp, tp, i32, vp, vp, sz, vp],
         "dlc_quantize_encode": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, vp, sz, vp],
         "dlc_quantize": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, u32, vp, sz, vp],
+        "dlc_quantize_static": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, u32, vp],
         "dlc_merge_outer_step": [vp, vp, vp, i64, i32, vp, vp, tp, i32, ctypes.c_double,
                                  ctypes.c_double, u32, vp],
         "dlc_quantize_bases": [vp, vp, i64, i32, vp, tp, i32, vp, vp, vp, vp, sz, vp],
@@ -302,6 +304,24 @@ def dlc_quantize(theta_g, theta_L, tensors, codes, codebook, range_io, workspace
     _check(_lib.dlc_quantize(_ptr(theta_g), _ptr(theta_L), stride, k, pres, arr, n,
                              _ptr(codes), _ptr(codebook), _ptr(range_io), flags, _ptr(workspace),
                              workspace.numel(), _stream(stream)))
+
+
+def dlc_quantize_static(theta_g, theta_L, tensors, codes, codebook, range_io, present=None, range_given=False,
+                        stream=None, debug_checks=False):
+    """dlc_quantize with the library's static device scratch as its workspace (no
+    workspace argument, nothing allocated): for callers that cannot allocate.
+    Calls that overlap on one device race on the scratch."""
+    c = _Checks()
+    k, stride = c.learners(theta_L, tensors)
+    _present_list(present, k)
+    c.global_(tensors, theta_g=theta_g)
+    c.outputs(k, len(tensors), codes, stride, codebook, range_io)
+    c.done()
+    arr, n = _tensors(tensors)
+    _buf, pres = _present(present, k)
+    flags = (DLC_RANGE_GIVEN if range_given else 0) | (DLC_DEBUG_CHECKS if debug_checks else 0)
+    _check(_lib.dlc_quantize_static(_ptr(theta_g), _ptr(theta_L), stride, k, pres, arr, n, _ptr(codes),
+                                    _ptr(codebook), _ptr(range_io), flags, _stream(stream)))
 
 
 def dlc_merge_outer_step(theta_g, momentum, codes, codebook, weights, tensors, lr=0.7, beta=0.9,

@@ -10,9 +10,16 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <numeric>
 #include <string>
 #include <vector>
+
+// Workspace of dlc_quantize_static, for callers that cannot allocate: one copy
+// per device, held until the process ends, shared by every such call on that
+// device (calls that overlap on one device race on it).  No call needs it to
+// start zeroed: every workspace slot is written before it is read.
+static __device__ __align__(256) unsigned char scratch[DLC_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -542,6 +549,91 @@ int32_t outer_cycle(float* theta_global, float* momentum, float* theta_learners,
   return ok();
 }
 
+// dlc_quantize after its flag checks, on the given workspace.
+int32_t quantize(const float* theta_global, const float* theta_learners, int64_t learner_stride,
+                 int32_t n_learners, const uint8_t* present, const dlc_tensor* tensors, int32_t n_tensors,
+                 uint8_t* codes, float* codebook, float* range, uint32_t flags, void* workspace,
+                 size_t workspace_bytes, void* hip_stream) {
+  const bool checks = (flags & DLC_DEBUG_CHECKS) != 0;
+  Common c;
+  int32_t rc = setup_quant(c, theta_global, theta_learners, learner_stride, n_learners, present, tensors,
+                           n_tensors, workspace, workspace_bytes, hip_stream);
+  if (rc != DLC_OK) return rc;
+  if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
+  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
+    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
+  c.args.range = reinterpret_cast<float4*>(range);
+  c.args.codes = codes;
+  c.args.codebook = codebook;
+  constexpr uint32_t kNone = 0xFFFFFFFFu;
+  if (checks) {
+    hipError_t e = dlc::launch_fill_u32(c.status, kNone, c.stream);
+    if (e != hipSuccess) return hip_fail(e, "status word");
+    c.args.status = c.status;
+  }
+  if ((flags & DLC_RANGE_GIVEN) == 0) {
+    rc = run_range(c);
+    if (rc != DLC_OK) return rc;
+  }
+  rc = run_encode(c);
+  if (rc != DLC_OK) return rc;
+  if (checks) {
+    uint32_t first = kNone;
+    hipError_t e = hipMemcpyAsync(&first, c.status, sizeof(first), hipMemcpyDeviceToHost, c.stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c.stream);
+    if (e != hipSuccess) return hip_fail(e, "debug checks");
+    if (first != kNone)
+      return fail(DLC_ERR_NON_FINITE, "learner " + std::to_string(first / (uint32_t)n_tensors) + ", tensor " +
+                                          std::to_string(first % (uint32_t)n_tensors) +
+                                          ": the pseudo-gradient holds NaN or Inf (the lowest such pair)");
+  }
+  return ok();
+}
+
+int32_t check_quantize_flags(uint32_t flags) {
+  if ((flags & ~(DLC_RANGE_GIVEN | DLC_DEBUG_CHECKS)) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
+  if ((flags & DLC_DEBUG_CHECKS) != 0 && (flags & DLC_RANGE_GIVEN) != 0)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "DLC_DEBUG_CHECKS needs the statistics stage (not DLC_RANGE_GIVEN)");
+  return DLC_OK;
+}
+
+// Workspace bytes of a quantize call with kp present learners (the layout setup_quant uses).
+size_t quantize_workspace(const dlc_tensor* tensors, int32_t n_tensors, int32_t kp) {
+  const Partition ps = stats_partition(tensors, n_tensors);
+  const Partition pe = encode_partition(tensors, n_tensors);
+  return workspace_layout(ps.n_slots, pe.n_slots, n_tensors, kp).total;
+}
+
+// The static scratch of dlc_quantize_static (the array is declared at the top of
+// this file).  Host code never uses the array's name as an address: its address
+// on each device comes from hipGetSymbolAddress, looked up once per device (the
+// first call on that device) with the device current, and kept.
+constexpr size_t kStaticScratchBytes = DLC_STATIC_SCRATCH_BYTES;
+static_assert(kStaticScratchBytes % 256 == 0, "whole 256-byte units");
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// This device's address of the scratch array.
+int32_t static_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "current device");
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLC_ERR_HIP, "device index beyond the scratch table");
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "static scratch address");
+  if (g_scratch_ptr[dev] == nullptr || !aligned256(g_scratch_ptr[dev]))
+    return fail(DLC_ERR_HIP, "static scratch address is not 256-byte aligned");
+  *ptr = g_scratch_ptr[dev];
+  return DLC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -620,43 +712,37 @@ int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
                      const dlc_tensor* tensors, int32_t n_tensors, uint8_t* codes,
                      float* codebook, float* range, uint32_t flags, void* workspace,
                      size_t workspace_bytes, void* hip_stream) {
-  if ((flags & ~(DLC_RANGE_GIVEN | DLC_DEBUG_CHECKS)) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
-  const bool checks = (flags & DLC_DEBUG_CHECKS) != 0;
-  if (checks && (flags & DLC_RANGE_GIVEN) != 0)
-    return fail(DLC_ERR_INVALID_ARGUMENT, "DLC_DEBUG_CHECKS needs the statistics stage (not DLC_RANGE_GIVEN)");
-  Common c;
-  int32_t rc = setup_quant(c, theta_global, theta_learners, learner_stride, n_learners, present, tensors,
-                           n_tensors, workspace, workspace_bytes, hip_stream);
+  int32_t rc = check_quantize_flags(flags);
   if (rc != DLC_OK) return rc;
-  if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
-  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
-    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
-  c.args.range = reinterpret_cast<float4*>(range);
-  c.args.codes = codes;
-  c.args.codebook = codebook;
-  constexpr uint32_t kNone = 0xFFFFFFFFu;
-  if (checks) {
-    hipError_t e = dlc::launch_fill_u32(c.status, kNone, c.stream);
-    if (e != hipSuccess) return hip_fail(e, "status word");
-    c.args.status = c.status;
-  }
-  if ((flags & DLC_RANGE_GIVEN) == 0) {
-    rc = run_range(c);
-    if (rc != DLC_OK) return rc;
-  }
-  rc = run_encode(c);
+  return quantize(theta_global, theta_learners, learner_stride, n_learners, present, tensors, n_tensors, codes,
+                  codebook, range, flags, workspace, workspace_bytes, hip_stream);
+}
+
+int32_t dlc_quantize_static(const float* theta_global, const float* theta_learners, int64_t learner_stride,
+                            int32_t n_learners, const uint8_t* present, const dlc_tensor* tensors,
+                            int32_t n_tensors, uint8_t* codes, float* codebook, float* range, uint32_t flags,
+                            void* hip_stream) {
+  int32_t rc = check_quantize_flags(flags);
   if (rc != DLC_OK) return rc;
-  if (checks) {
-    uint32_t first = kNone;
-    hipError_t e = hipMemcpyAsync(&first, c.status, sizeof(first), hipMemcpyDeviceToHost, c.stream);
-    if (e == hipSuccess) e = hipStreamSynchronize(c.stream);
-    if (e != hipSuccess) return hip_fail(e, "debug checks");
-    if (first != kNone)
-      return fail(DLC_ERR_NON_FINITE, "learner " + std::to_string(first / (uint32_t)n_tensors) + ", tensor " +
-                                          std::to_string(first % (uint32_t)n_tensors) +
-                                          ": the pseudo-gradient holds NaN or Inf (the lowest such pair)");
-  }
-  return ok();
+  // the scratch this call needs, checked before any HIP call
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  rc = check_tensors(tensors, n_tensors, learner_stride, true);
+  if (rc != DLC_OK) return rc;
+  int32_t kp = 0;
+  for (int32_t i = 0; i < n_learners; ++i) kp += present == nullptr || present[i] != 0 ? 1 : 0;
+  if (kp == 0) return fail(DLC_ERR_NO_QUORUM, "no learner is present");
+  const size_t need = quantize_workspace(tensors, n_tensors, kp);
+  if (need > kStaticScratchBytes)
+    return fail(DLC_ERR_WORKSPACE, "the call needs " + std::to_string(need) + " bytes of scratch, more than the " +
+                                       std::to_string(kStaticScratchBytes) +
+                                       " of the static scratch: split it into smaller fragments, or pass a "
+                                       "workspace to dlc_quantize");
+  void* ws = nullptr;
+  rc = static_scratch(&ws);
+  if (rc != DLC_OK) return rc;
+  return quantize(theta_global, theta_learners, learner_stride, n_learners, present, tensors, n_tensors, codes,
+                  codebook, range, flags, ws, kStaticScratchBytes, hip_stream);
 }
 
 int32_t dlc_quantize_bases(const float* const* bases, const float* theta_learners, int64_t learner_stride,

@@ -173,6 +173,32 @@ int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
                      size_t workspace_bytes, void* hip_stream);
 
 /*
+ * dlc_quantize_static -- dlc_quantize for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same call, the same results bit for bit, with no
+ * workspace argument.  Its workspace is the library's static scratch, a device
+ * array of DLC_STATIC_SCRATCH_BYTES bytes that each device the library runs on
+ * holds until the process ends; the call allocates nothing (no hipMalloc, no
+ * hipFree, no allocating library routine).
+ *   - A call whose workspace (dlc_workspace_bytes for its present learners)
+ *     exceeds DLC_STATIC_SCRATCH_BYTES returns DLC_ERR_WORKSPACE before anything
+ *     is enqueued: split it into smaller fragments, or use dlc_quantize.
+ *   - Every call on one device shares that device's scratch, which keeps the last
+ *     call's contents (no call needs it cleared).  Calls that overlap on one
+ *     device -- on different streams or threads without ordering -- race on it:
+ *     the caller orders them.
+ *   - The first call on a device looks up that device's scratch address (the
+ *     device must be current); a failure there returns DLC_ERR_HIP.
+ * Arguments, flags and errors otherwise as dlc_quantize.
+ */
+#define DLC_STATIC_SCRATCH_BYTES 67108864u /* 64 MiB */
+
+int32_t dlc_quantize_static(const float* theta_global, const float* theta_learners, int64_t learner_stride,
+                            int32_t n_learners, const uint8_t* present, const dlc_tensor* tensors,
+                            int32_t n_tensors, uint8_t* codes, float* codebook, float* range, uint32_t flags,
+                            void* hip_stream);
+
+/*
  * dlc_quantize_bases -- dlc_quantize for learners that started from different
  * versions of the global parameters (Decoupled DiLoCo digest, "fault tolerance":
  * learners run asynchronously and may report against an older global fragment).

@@ -42,7 +42,7 @@ def test_header_constants_match_binding():
     for name in ("DLC_OK", "DLC_ERR_INVALID_ARGUMENT", "DLC_ERR_ALIGNMENT", "DLC_ERR_NO_QUORUM",
                  "DLC_ERR_WORKSPACE", "DLC_ERR_HIP", "DLC_MAX_LEARNERS", "DLC_N_BUCKETS",
                  "DLC_ALIGN_ELEMS", "DLC_RANGE_FIELDS", "DLC_RANGE_GIVEN", "DLC_BROADCAST", "DLC_TWO_LANES",
-                 "DLC_MAX_LANES", "DLC_ERR_NON_FINITE", "DLC_DEBUG_CHECKS"):
+                 "DLC_MAX_LANES", "DLC_ERR_NON_FINITE", "DLC_DEBUG_CHECKS", "DLC_STATIC_SCRATCH_BYTES"):
         m = re.search(rf"#define {name} \(?(-?\d+)u?\)?", text)
         assert m and int(m.group(1)) == getattr(dlc, name), name
 
@@ -95,6 +95,22 @@ def quantize(k=2, spec=((0, 0, 4096),), stride=4096, theta=FAKE, present=None, w
         buf = (ctypes.c_uint8 * k)(*present)
         pres = ctypes.cast(buf, ctypes.c_void_p)
     return L.dlc_quantize(theta, FAKE, stride, k, pres, arr, n, codes, FAKE, FAKE, flags, ws, ws_bytes, None)
+
+
+def quantize_static(k=2, spec=((0, 0, 4096),), stride=4096, present=None, flags=0):
+    """dlc_quantize_static with fake pointers: only calls whose arguments or scratch
+    size are refused before the device is touched belong here."""
+    arr, n = tens(spec)
+    pres = None
+    if present is not None:
+        buf = (ctypes.c_uint8 * k)(*present)
+        pres = ctypes.cast(buf, ctypes.c_void_p)
+    return L.dlc_quantize_static(FAKE, FAKE, stride, k, pres, arr, n, FAKE, FAKE, FAKE, flags, None)
+
+
+# a call whose workspace exceeds the static scratch: one tensor of 2^27 elements
+# (8192 encode blocks of 4 tiles) with 16 learners needs 256 MiB of histograms
+BIG_STATIC = dict(k=16, spec=((0, 0, 1 << 27),), stride=1 << 27)
 
 
 def quantize_bases(bases=(FAKE, FAKE), present=None, ws_bytes=16):
@@ -272,6 +288,13 @@ def test_rda_and_ring_workspace_sizes():
     (lambda: cycle_lanes(weights=((1.0, 1.0), (0.0, 0.0))), dlc.DLC_ERR_NO_QUORUM),
     (lambda: cycle_lanes(ws_bytes=64), dlc.DLC_ERR_WORKSPACE),
     (lambda: lanes_ws_short(), dlc.DLC_ERR_WORKSPACE),
+    (lambda: quantize_static(**BIG_STATIC), dlc.DLC_ERR_WORKSPACE),
+    (lambda: quantize_static(**BIG_STATIC, present=[1] * 15 + [0]), dlc.DLC_ERR_WORKSPACE),
+    (lambda: quantize_static(k=65), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize_static(flags=16), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize_static(flags=dlc.DLC_DEBUG_CHECKS | dlc.DLC_RANGE_GIVEN), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize_static(spec=((0, 0, 4097),)), dlc.DLC_ERR_INVALID_ARGUMENT),
+    (lambda: quantize_static(present=[0, 0]), dlc.DLC_ERR_NO_QUORUM),
 ])
 def test_argument_errors(call, code):
     assert call() == code
@@ -299,3 +322,13 @@ def test_the_product_path_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f), encoding="utf-8").read()
                 assert not re.search(r"\boracle\b", text), os.path.join(dirpath, f)
+
+
+def test_static_scratch_limit_matches_the_workspace_sizes():
+    """The static-scratch call takes exactly the calls whose workspace fits it."""
+    assert dlc.DLC_STATIC_SCRATCH_BYTES == 64 << 20
+    need = dlc.dlc_workspace_bytes(16, [(0, 0, 1 << 27)])
+    assert need > dlc.DLC_STATIC_SCRATCH_BYTES
+    assert "static scratch" in (quantize_static(**BIG_STATIC) and dlc.dlc_last_error())
+    # the 135M set's largest fragment (its 28M-param embedding) at K = 4 fits
+    assert dlc.dlc_workspace_bytes(4, [(0, 0, 49152 * 576)]) <= dlc.DLC_STATIC_SCRATCH_BYTES
