@@ -284,6 +284,18 @@ def build_global(cfg: Config, tensor_ids: Sequence[int], device, step: int = 0,
     return theta, mom, list(offsets)
 
 
+def learner_delta(cfg: Config, tensor: int, learner: int, step: int, sigma: float, device) -> torch.Tensor:
+    """Learner `learner`'s pseudo-gradient draw for one tensor at one step: the
+    draw build_learners subtracts from theta_g (fp32, on `device`)."""
+    s = cfg.tensors[tensor]
+    if s.kind == "const":
+        const_rank = sum(1 for t in range(tensor) if cfg.tensors[t].kind == "const")
+        c = const_delta_value(cfg, tensor, learner, const_rank)
+        return torch.full((s.numel,), c, dtype=torch.float32, device=device)
+    g = generator(seed_of(cfg.key, step, tensor, ROLE_LEARNER0 + learner), device)
+    return draw_delta(cfg, s, sigma, g, device)
+
+
 def build_learners(cfg: Config, tensor_ids: Sequence[int], theta_g: torch.Tensor,
                    offsets: Sequence[int], device, step: int = 0,
                    present: Optional[Sequence[int]] = None,
