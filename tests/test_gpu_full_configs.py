@@ -323,3 +323,76 @@ def test_c3_resume_from_a_checkpoint_is_bit_identical():
     print("[c3 resume] five steps, checkpoint, five steps done", flush=True)
     assert torch.equal(theta_a, theta_b) and torch.equal(mom_a, mom_b)
     assert not torch.equal(theta_a, workloads.build_global(cfg, ids, DEV)[0])
+
+
+def test_c2_resume_mid_cycle_is_bit_identical():
+    """The 135M set's 24-fragment cycle (dlc_outer_cycle, one stream) against the
+    same cycle interrupted after fragment 11: theta, momentum and the fragment
+    cursor saved and loaded (torch.save / torch.load with weights_only), then
+    fragments 12..23 through dlc_quantize + dlc_merge_outer_step, bit for bit."""
+    import io
+
+    cfg = workloads.config("c2")
+    ids = list(range(len(cfg.tensors)))
+    inp = workloads.fragment_inputs(cfg, ids, DEV)
+    k, stride = inp.theta_L.shape
+    frag, _ = dlc.dlc_fragment_plan([s.numel for s in cfg.tensors], 24)
+    tens, first, order = dlc.group_by_fragment(inp.tensors, frag, 24)
+    w = [list(inp.weights) for _ in range(24)]
+    codes, cb, rng = dlc.outputs_for(k, stride, len(tens), DEV)
+    ws = torch.empty(max(256, dlc.dlc_cycle_workspace_bytes(k, tens, first)), dtype=torch.uint8, device=DEV)
+    theta_a, mom_a = inp.theta_g.clone(), inp.momentum.clone()
+    dlc.dlc_outer_cycle(theta_a, mom_a, inp.theta_L, tens, first, w, codes, cb, rng, ws, cfg.lr, cfg.beta)
+    torch.cuda.synchronize()
+
+    theta_b, mom_b = inp.theta_g.clone(), inp.momentum.clone()
+
+    def fragments(theta, mom, lo, hi):
+        for p in range(lo, hi):
+            sel = tens[first[p]:first[p + 1]]
+            if not sel:
+                continue
+            sub = workloads.StepInputs(theta, mom, inp.theta_L, sel, inp.weights, inp.present, [], stride)
+            run_call(sub, theta, mom, cfg.lr, cfg.beta)
+
+    fragments(theta_b, mom_b, 0, 12)
+    buf = io.BytesIO()
+    torch.save({"theta": theta_b.cpu(), "momentum": mom_b.cpu(), "next_fragment": 12}, buf)
+    del theta_b, mom_b
+    buf.seek(0)
+    ck = torch.load(buf, weights_only=True)
+    theta_b, mom_b = ck["theta"].to(DEV), ck["momentum"].to(DEV)
+    fragments(theta_b, mom_b, ck["next_fragment"], 24)
+    torch.cuda.synchronize()
+    assert torch.equal(theta_a, theta_b) and torch.equal(mom_a, mom_b)
+    assert not torch.equal(theta_a, inp.theta_g)
+
+
+@pytest.mark.parametrize("key", ["c1", "c3", "c4_median", "c5k16"])
+def test_full_size_calls_are_deterministic(key):
+    """The benchmark's call shape twice on the same inputs: codes, codebooks,
+    ranges, theta and momentum bit-identical (integer histograms and fixed-order
+    reductions: no result depends on the order of atomics or of block completion)."""
+    if key == "c4_median":
+        cfg = workloads.config("c4")
+        ids, p = fragment_ids(cfg, "median")
+    elif key == "c5k16":
+        cfg = workloads.config("c5k16")
+        ids, p = fragment_ids(cfg, "median")
+    else:
+        cfg = workloads.config(key)
+        ids, p = list(range(len(cfg.tensors))), 0
+    inp = workloads.fragment_inputs(cfg, ids, DEV, fragment=p)
+    outs = []
+    for _ in range(2):
+        theta, mom = inp.theta_g.clone(), inp.momentum.clone()
+        codes, cb, rng = run_call(inp, theta, mom, cfg.lr, cfg.beta)
+        outs.append((codes, cb, rng, theta, mom))
+    (c0, b0, r0, t0, m0), (c1, b1, r1, t1, m1) = outs
+    assert torch.equal(t0, t1) and torch.equal(m0, m1)
+    assert torch.equal(b0[[i for i, q in enumerate(inp.present) if q]], b1[[i for i, q in enumerate(inp.present) if q]])
+    assert torch.equal(r0[[i for i, q in enumerate(inp.present) if q]], r1[[i for i, q in enumerate(inp.present) if q]])
+    for i, q in enumerate(inp.present):
+        if q:
+            for (_, lo, n) in inp.tensors:
+                assert torch.equal(c0[i, lo:lo + n], c1[i, lo:lo + n])
