@@ -3,6 +3,9 @@
 The functions here carry the C ABI's names (include/dlc.h) and only marshal
 arguments: torch tensors supply device memory, torch's current HIP stream is the
 default stream, and every step of the computation runs in the library's kernels.
+Before each call the binding checks the buffers it passes (dtype, contiguity,
+extent against the tensor list, one device, a GPU) and the lengths of weight and
+presence lists, so no caller mistake reaches a kernel as an out-of-bounds access.
 Importing this package fails loudly if the library has not been built
 (``python diloco_outer_step_amd/build.py``).
 """
