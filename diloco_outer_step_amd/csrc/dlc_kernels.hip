@@ -371,6 +371,12 @@ __device__ __forceinline__ double uniform_f64(double v) {
 //   bias = kHistBias + ceil(max(0, -e) * 2^s)
 // and s is the largest value <= kHistFracBits that keeps the highest, q + bias,
 // below 2^27: (max(1, e) + max(0, -e)) * 2^s + 2 * kHistBias < 2^27 (normally 26).
+// Such an s exists for every tensor whose clip bounds are finite: a non-constant
+// fp32 tensor of n <= 2^32 elements has sigma >= ulp(mu) / sqrt(n), so
+// (hi - lo) / wd <= 256 + 21 * 2^-23 * |mu| / sigma + 1 < 1.5e6 (a constant tensor,
+// or one whose wd underflows, takes the zero-variance path).  Infinite bounds
+// (|mu| + 6 sigma beyond the fp32 range) are outside the contract, as for the
+// statistics.
 struct HistFormat {
   int s;
   double bias;  // an integer

@@ -142,7 +142,8 @@ int32_t dlc_quantize_range(const float* theta_global, const float* theta_learner
  *   wd * 2^-27 of the exact mean before its fp32 rounding (and independent of the
  *   order in which elements are accumulated).
  *   If wd is not a normal fp32 (zero variance), every code is 0 and every
- *   codebook entry is `mean`.
+ *   codebook entry is `mean`.  lo and hi must be finite (pseudo-gradients with
+ *   |mu| + 6 sigma beyond the fp32 range are outside the contract).
  *   codes     device uint8 [n_learners][learner_stride], written at the tensors'
  *             ranges of present learners
  *   codebook  device fp32 [n_learners][n_tensors][256], written for present learners
