@@ -290,8 +290,10 @@ def native_cycle(key, device, reps=5, warmup=2):
     """The whole fragment cycle through dlc_outer_cycle: quantize and merge on one
     stream, on two overlapped streams, on two streams with the update sent back to
     the learners (dlc_broadcast after each merge), with consecutive fragments on
-    alternating lanes (DLC_TWO_LANES), on three lanes (dlc_outer_cycle_lanes), and
-    the three-lane cycle captured in a HIP graph and replayed."""
+    alternating lanes (DLC_TWO_LANES), on three and four lanes (dlc_outer_cycle_lanes),
+    and the three- and four-lane cycles captured in a HIP graph and replayed.  Four
+    lanes match the four hardware queues a process gets here; more lanes share them
+    and measured slower."""
     import statistics
     import torch
     import diloco_outer_step_amd as dlc
@@ -304,21 +306,22 @@ def native_cycle(key, device, reps=5, warmup=2):
     k, stride = inp.theta_L.shape
     weights = [list(inp.weights)] * cfg.n_fragments
     codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), device)
-    ws = torch.empty(max(256, 3 * dlc.dlc_cycle_workspace_bytes(k, grouped, first)), dtype=torch.uint8,
+    ws = torch.empty(max(256, 4 * (dlc.dlc_cycle_workspace_bytes(k, grouped, first) + 256)), dtype=torch.uint8,
                      device=device)
     theta, mom, theta_L = inp.theta_g.clone(), inp.momentum.clone(), inp.theta_L.clone()
     qs = torch.cuda.current_stream()
     ms = torch.cuda.Stream()
     n_params = sum(n for _, _, n in grouped)
     out = {}
-    third = torch.cuda.Stream()
+    lane_streams = [qs, ms, torch.cuda.Stream(), torch.cuda.Stream()]
     for name, merge_stream, bc, lanes in (("one_stream", qs, False, False), ("two_streams", ms, False, False),
                                           ("two_streams_send_back", ms, True, False),
-                                          ("two_lanes", ms, False, True), ("three_lanes", ms, False, 3)):
+                                          ("two_lanes", ms, False, True), ("three_lanes", ms, False, 3),
+                                          ("four_lanes", ms, False, 4)):
         def run():
-            if lanes == 3:
+            if lanes in (3, 4):
                 dlc.dlc_outer_cycle_lanes(theta, mom, inp.theta_L, grouped, first, weights, codes, cb, rng, ws,
-                                          [qs, ms, third])
+                                          lane_streams[:lanes])
                 return
             dlc.dlc_outer_cycle(theta, mom, theta_L if bc else inp.theta_L, grouped, first, weights, codes, cb, rng,
                                 ws, broadcast=bc, quantize_stream=qs, merge_stream=merge_stream, two_lanes=lanes)
@@ -337,29 +340,34 @@ def native_cycle(key, device, reps=5, warmup=2):
         b = (24 + 10 * k + (4 + 4 * k if bc else 0)) * n_params
         out[name] = dict(cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3), hbm_gbps=b / (ms_ * 1e-3) / 1e9,
                          bytes_per_param=b // n_params)
-    # the three-lane cycle captured once in a HIP graph and replayed: no host launch cost
-    graph, side, others = torch.cuda.CUDAGraph(), torch.cuda.Stream(), [torch.cuda.Stream(), torch.cuda.Stream()]
-    side.wait_stream(qs)
-    with torch.cuda.stream(side):
-        with torch.cuda.graph(graph, stream=side):
-            dlc.dlc_outer_cycle_lanes(theta, mom, inp.theta_L, grouped, first, weights, codes, cb, rng, ws,
-                                      [side] + others)
-    qs.wait_stream(side)
-    for _ in range(warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(qs)
-        graph.replay()
-        e1.record(qs)
+    # the three- and four-lane cycles captured once in a HIP graph and replayed: no
+    # host launch cost
+    for n_lanes in (3, 4):
+        graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        others = [torch.cuda.Stream() for _ in range(n_lanes - 1)]
+        side.wait_stream(qs)
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                dlc.dlc_outer_cycle_lanes(theta, mom, inp.theta_L, grouped, first, weights, codes, cb, rng, ws,
+                                          [side] + others)
+        qs.wait_stream(side)
+        for _ in range(warmup):
+            graph.replay()
         torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    ms_ = statistics.median(ts)
-    b = (24 + 10 * k) * n_params
-    out["three_lanes_graph"] = dict(cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3),
-                                    hbm_gbps=b / (ms_ * 1e-3) / 1e9, bytes_per_param=b // n_params)
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(qs)
+            graph.replay()
+            e1.record(qs)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ms_ = statistics.median(ts)
+        b = (24 + 10 * k) * n_params
+        out[("three" if n_lanes == 3 else "four") + "_lanes_graph"] = dict(
+            cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3), hbm_gbps=b / (ms_ * 1e-3) / 1e9,
+            bytes_per_param=b // n_params)
+        del graph
     out["workload"] = cfg.title
     out["fragments"] = cfg.n_fragments
     return out

@@ -53,12 +53,13 @@ def test_captured_step_replays_the_eager_step():
         assert torch.equal(th, th_e) and torch.equal(mo, mo_e), rep
 
 
-@pytest.mark.parametrize("mode", ["two_streams", "two_lanes", "three_lanes"])
+@pytest.mark.parametrize("mode", ["two_streams", "two_lanes", "three_lanes", "four_lanes"])
 def test_captured_cycle_replays_the_eager_cycle(mode):
     """A whole fragment cycle on two streams (the second joins the capture through
-    the cycle's own events), on two lanes, and on three lanes through
+    the cycle's own events), on two lanes, and on three and four lanes through
     dlc_outer_cycle_lanes, captured once and replayed."""
     two_lanes = mode == "two_lanes"
+    n_lanes = {"three_lanes": 3, "four_lanes": 4}.get(mode, 0)
     sizes = [4096] * 6 + [64 * 1000 + 5] * 3 + [1 << 17, 777]
     cfg = workloads.custom("graph_cycle", sizes, 4)
     inp = workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV)
@@ -66,7 +67,7 @@ def test_captured_cycle_replays_the_eager_cycle(mode):
     frag, _ = dlc.dlc_fragment_plan(sizes, 5)
     grouped, first, _ = dlc.group_by_fragment(inp.tensors, frag, 5)
     weights = [list(inp.weights)] * 5
-    need = dlc.dlc_cycle_workspace_bytes(k, grouped, first) * 3
+    need = (dlc.dlc_cycle_workspace_bytes(k, grouped, first) + 256) * 4
 
     def buffers():
         codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), DEV)
@@ -76,20 +77,20 @@ def test_captured_cycle_replays_the_eager_cycle(mode):
     codes_e, cb_e, rng_e, ws_e, th_e, mo_e, tl_e = buffers()
 
     def cycle(th, mo, tl, codes, cb, rng, ws, first_stream, others):
-        if mode == "three_lanes":
+        if n_lanes:
             dlc.dlc_outer_cycle_lanes(th, mo, tl, grouped, first, weights, codes, cb, rng, ws,
-                                      [first_stream] + others, broadcast=True)
+                                      [first_stream] + others[:n_lanes - 1], broadcast=True)
         else:
             dlc.dlc_outer_cycle(th, mo, tl, grouped, first, weights, codes, cb, rng, ws, broadcast=True,
                                 quantize_stream=first_stream, merge_stream=others[0], two_lanes=two_lanes)
 
     cycle(th_e, mo_e, tl_e, codes_e, cb_e, rng_e, ws_e, torch.cuda.current_stream(),
-          [torch.cuda.Stream(), torch.cuda.Stream()])
+          [torch.cuda.Stream() for _ in range(3)])
     torch.cuda.synchronize()
 
     codes, cb, rng, ws, th, mo, tl = buffers()
     graph = torch.cuda.CUDAGraph()
-    side, others = torch.cuda.Stream(), [torch.cuda.Stream(), torch.cuda.Stream()]
+    side, others = torch.cuda.Stream(), [torch.cuda.Stream() for _ in range(3)]
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
