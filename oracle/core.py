@@ -216,6 +216,11 @@ def merge(codes_per_learner, codebook_per_learner, w_hat):
     return g
 
 
+# Averaged directions no longer than this share of their largest possible norm are
+# rounding noise of directions that cancel (see rda_merge).
+RDA_NULL_DIRECTION = 2.0 ** -40
+
+
 def rda_merge(codes_per_learner, codebook_per_learner, w_hat):
     """Radial-Directional Averaging (Decoupled DiLoCo digest, "architecture", the
     second engineering detail, and "fault tolerance" item 3): instead of a plain
@@ -230,9 +235,15 @@ def rda_merge(codes_per_learner, codebook_per_learner, w_hat):
         d   = sum_i w_hat_i u_i          the averaged direction
         g   = r * d / ||d||_2            (g = 0 when d = 0)
 
-    so g has the averaged norm and points along the averaged direction."""
+    so g has the averaged norm and points along the averaged direction.
+    ||d|| is at most W = sum of w_hat_i over the learners with r_i > 0.  Directions
+    that cancel in real arithmetic (d = 0, e.g. constant tensors moved by opposite
+    amounts under equal weights) leave only rounding noise in d, about K 2^-53 W,
+    which points nowhere in particular; d therefore counts as zero when
+    ||d|| <= RDA_NULL_DIRECTION * W."""
     n = len(codes_per_learner[0])
     r = 0.0
+    w_moved = 0.0
     d = None
     for codes, cb, w in zip(codes_per_learner, codebook_per_learner, w_hat):
         if w == 0.0:
@@ -241,12 +252,13 @@ def rda_merge(codes_per_learner, codebook_per_learner, w_hat):
         r_i = float(np.sqrt(np.sum(x * x)))
         r += w * r_i
         if r_i > 0.0:
+            w_moved += w
             term = w * (x / r_i)
             d = term if d is None else d + term
     if d is None:
         return np.zeros(n, np.float64)
     d_norm = float(np.sqrt(np.sum(d * d)))
-    if d_norm == 0.0:
+    if d_norm <= RDA_NULL_DIRECTION * w_moved:
         return np.zeros(n, np.float64)
     return r * (d / d_norm)
 

@@ -83,6 +83,14 @@ def _rda_unweighted_norm(codes_per_learner, codebook_per_learner, w_hat):
     return r * d / np.sqrt(np.sum(d * d))
 
 
+def _rda_exact_zero_test(codes_per_learner, codebook_per_learner, w_hat):
+    xs, rs = _rda_parts(codes_per_learner, codebook_per_learner, w_hat)
+    r = sum(w * ri for (w, _), ri in zip(xs, rs))
+    d = sum(w * (x / ri) for (w, x), ri in zip(xs, rs) if ri > 0)
+    dn = float(np.sqrt(np.sum(d * d)))
+    return r * d / dn if dn > 0.0 else np.zeros_like(d)
+
+
 def _ring_wrong_direction(rank, hop, k):
     return (rank + hop) % k
 
@@ -150,6 +158,8 @@ MUTATIONS = {
     "rda_plain_mean": (lambda mp: _patch(mp, "rda_merge", _rda_plain_mean),
                        [pins.test_rda_two_equal_weights_bisect_the_angle,
                         lambda: pins.test_rda_orthogonal_halves_closed_form(3.0, 1.0)]),
+    "rda_null_direction_tested_exactly": (lambda mp: _patch(mp, "rda_merge", _rda_exact_zero_test),
+                                          [lambda: pins.test_rda_balanced_constant_learners_give_zero(2)]),
     "rda_unweighted_norm": (lambda mp: _patch(mp, "rda_merge", _rda_unweighted_norm),
                             [lambda: pins.test_rda_norm_is_the_weighted_mean_norm(0)]),
     "ring_chunks_travel_the_wrong_way": (lambda mp: _patch(mp, "ring_sent_chunk", _ring_wrong_direction),

@@ -729,6 +729,45 @@ def test_rda_opposite_learners_cancel():
     assert np.all(g == 0.0)
 
 
+def _rda_constants(values, n=5000):
+    """codes / codebooks of learners whose dequantized tensors are the given constants."""
+    codes, cbs = [], []
+    for v in values:
+        q = oracle.quantize_tensor(np.full(n, np.float32(v), np.float32))
+        codes.append(q["codes"])
+        cbs.append(q["codebook"])
+    return codes, cbs
+
+
+@pytest.mark.parametrize("seed", [2, 3, 4, 5])
+def test_rda_balanced_constant_learners_give_zero(seed):
+    # Twelve learners moved a tensor by constants, six up and six down, under equal
+    # weights: every u_i is +-1/sqrt(n) times the same vector, so d = 0 exactly in
+    # real arithmetic and g = 0.  (In fp64, with n not a power of two, the norms
+    # round and d keeps ~1e-16 of noise, which an exact-zero test would normalize
+    # into a full-size step.)
+    rng = np.random.default_rng(seed)
+    signs = np.array([1.0] * 6 + [-1.0] * 6)
+    rng.shuffle(signs)
+    codes, cbs = _rda_constants(signs * 10.0 ** rng.uniform(-5, -3, 12))
+    g = oracle.rda_merge(codes, cbs, [1.0 / 12] * 12)
+    assert np.all(g == 0.0)
+
+
+@pytest.mark.parametrize("eps", [1e-3, 1e-6])
+def test_rda_nearly_opposite_constants_closed_form(eps):
+    # x1 = c1, x2 = -c2 (constants) with weights 1/2 + eps and 1/2 - eps: d = 2 eps
+    # times the unit vector of ones, so g = w1 c1 + w2 c2 on every element (the
+    # averaged norm along the heavier learner's direction), however small eps is
+    # as long as d is more than rounding noise.
+    c1, c2 = 3e-4, 7e-4
+    codes, cbs = _rda_constants([c1, -c2])
+    w1, w2 = 0.5 + eps, 0.5 - eps
+    g = oracle.rda_merge(codes, cbs, [w1, w2])
+    x1, x2 = float(np.float32(c1)), float(np.float32(c2))
+    np.testing.assert_allclose(g, w1 * x1 + w2 * x2, rtol=1e-12)
+
+
 def test_rda_zero_learner_adds_no_direction():
     # r = w1 r1 and d = w1 u1, so g = w1 x1: a learner that did not move dilutes
     # the norm by its weight and nothing else.
