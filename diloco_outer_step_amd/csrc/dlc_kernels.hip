@@ -1012,8 +1012,13 @@ __global__ __launch_bounds__(kMergeBlock) __attribute__((amdgpu_waves_per_eu(4))
 
 // k_rda_coef: one block per tensor.  ||d||^2 = the tensor's block sums of the
 // squared averaged direction (strided per thread, then a fixed tree);
-// r = sum_i w_hat_i ||x_i|| in learner order; coef_i = a_i * r / ||d|| (all 0
-// when ||d|| = 0, so g = 0).
+// r = sum_i w_hat_i ||x_i|| in learner order; coef_i = a_i * r / ||d||, all 0
+// (g = 0) when d counts as zero: ||d|| <= kRdaNullDirection * W, W = the summed
+// w_hat_i of the learners with ||x_i|| > 0, the largest ||d|| can be.  Directions
+// that cancel in real arithmetic leave only about K 2^-53 W of rounding noise in
+// d, which points nowhere in particular.
+constexpr double kRdaNullDirection = 0x1p-40;
+
 __global__ __launch_bounds__(kBuckets) void k_rda_coef(const MergeArgs a, const LaunchGeom g) {
   __shared__ double st[kBuckets];
   __shared__ double scale;
@@ -1025,9 +1030,14 @@ __global__ __launch_bounds__(kBuckets) void k_rda_coef(const MergeArgs a, const 
   const size_t trow = (size_t)g.row_base + g.t_base + t;
   const int kp = a.n_present;
   if (threadIdx.x == 0) {
-    double r = 0.0;
-    for (int k = 0; k < kp; ++k) r += a.w_hat[k] * __builtin_sqrt(a.norm2[(size_t)a.learner[k] * g.n_tensors_call + trow]);
-    scale = d2 > 0.0 ? r / __builtin_sqrt(d2) : 0.0;
+    double r = 0.0, moved = 0.0;
+    for (int k = 0; k < kp; ++k) {
+      const double n2 = a.norm2[(size_t)a.learner[k] * g.n_tensors_call + trow];
+      r += a.w_hat[k] * __builtin_sqrt(n2);
+      if (n2 > 0.0) moved += a.w_hat[k];
+    }
+    const double dn = __builtin_sqrt(d2);
+    scale = dn > kRdaNullDirection * moved ? r / dn : 0.0;
   }
   __syncthreads();
   for (int k = threadIdx.x; k < kp; k += kBuckets) a.coef[trow * kp + k] = scale * rda_unit_weight(a, g, trow, k);

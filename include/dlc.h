@@ -392,6 +392,9 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
  *   d = sum_i w_hat_i x_i / ||x_i||                the averaged direction
  *                                                  (a learner with x_i = 0 adds none)
  *   g = r d / ||d||                                (g = 0 when d = 0)
+ * where d counts as zero when ||d|| <= 2^-40 W, W = sum of w_hat_i over the
+ * learners with x_i != 0 (the largest ||d|| can be): directions that cancel in
+ * real arithmetic leave only rounding noise in d;
  * then v <- beta v + g; theta <- theta - lr (g + beta v) as dlc_merge_outer_step.
  * Learners with weight 0 are absent: neither quantized nor read, and their rows
  * of every output are left untouched.  Results agree with the fp64 definition up

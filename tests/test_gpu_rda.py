@@ -163,6 +163,29 @@ def test_identical_learners_are_the_star_step():
     assert d.max() <= 2
 
 
+def test_balanced_constant_learners_cancel():
+    """Twelve learners move tensor 0 by constants, six up and six down, under equal
+    weights: their directions cancel in real arithmetic, so g = 0 there and the
+    step is the pure momentum step (the averaged direction left by rounding counts
+    as zero); tensor 1 moves normally.  Tensor 0 has a size that is no power of
+    two, so the norms round."""
+    k, sizes = 12, [114687, 5000]
+    inp = make_inputs(31, k, sizes, [1.0] * k)
+    off, loff, n = inp.tensors[0]
+    inp.theta_g[off:off + n] = 0.5
+    rng = np.random.default_rng(31)
+    signs = np.array([1.0] * 6 + [-1.0] * 6)
+    rng.shuffle(signs)
+    for i, c in enumerate(signs * 10.0 ** rng.uniform(-5, -3, k)):
+        inp.theta_L[i, loff:loff + n] = float(np.float32(0.5) - np.float32(c))
+    theta0, mom0 = parity.host(inp.theta_g), parity.host(inp.momentum)
+    gpu = gpu_rda(inp)
+    check_merge_on_gpu_codes(gpu, inp, theta0, mom0)
+    th_o, mo_o = oracle.nesterov(theta0[off:off + n], mom0[off:off + n], np.zeros(n), LR, BETA)
+    assert np.array_equal(parity.host(gpu["momentum"])[off:off + n], mo_o)
+    assert np.array_equal(parity.host(gpu["theta"])[off:off + n], th_o)
+
+
 @pytest.mark.slow
 def test_rda_full_1b_set_sampled_tensors():
     cfg = workloads.config("c3")
