@@ -78,6 +78,24 @@ def case_inputs(name):
         return workloads.StepInputs(theta, mom, theta_L, tensors, [1.0, 2.0, 1.0], [1, 1, 1], [0, 1, 2], stride)
     if name == "above_hi_mean_dominated_k2":
         return above_hi_inputs()
+    if name == "tiny_values_k3":
+        # parameters near the bottom of the fp32 range: learner 0's pseudo-gradients
+        # are subnormal (its bucket width underflows: the zero-variance path), learner
+        # 1's width lands just above FLT_MIN, learner 2's values are tiny but normal;
+        # every subtraction must keep subnormal results (no flush to zero)
+        sizes = [5000, 4096 * 2 + 7, 64]
+        tensors, stride = [], 0
+        for n in sizes:
+            tensors.append((stride, stride, n))
+            stride += (n + 63) // 64 * 64
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(77)
+        theta = torch.randn(stride, generator=gen, device=DEV) * 1e-36
+        mom = torch.zeros(stride, device=DEV)
+        theta_L = torch.empty((3, stride), device=DEV)
+        for i, scale in enumerate([2e-39, 4e-37, 3e-35]):
+            theta_L[i] = theta - torch.randn(stride, generator=gen, device=DEV) * scale
+        return workloads.StepInputs(theta, mom, theta_L, tensors, [1.0, 1.0, 2.0], [1, 1, 1], [0, 1, 2], stride)
     raise KeyError(name)
 
 
@@ -101,7 +119,7 @@ def above_hi_inputs():
 
 
 CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const", "sparse_k8",
-         "max_learners_k64", "mean_dominated_k3", "above_hi_mean_dominated_k2"]
+         "max_learners_k64", "mean_dominated_k3", "above_hi_mean_dominated_k2", "tiny_values_k3"]
 
 
 @pytest.mark.parametrize("name", CASES)
