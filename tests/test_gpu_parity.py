@@ -96,6 +96,22 @@ def case_inputs(name):
         for i, scale in enumerate([2e-39, 4e-37, 3e-35]):
             theta_L[i] = theta - torch.randn(stride, generator=gen, device=DEV) * scale
         return workloads.StepInputs(theta, mom, theta_L, tensors, [1.0, 1.0, 2.0], [1, 1, 1], [0, 1, 2], stride)
+    if name == "huge_values_k2":
+        # parameters near the top of the fp32 range (clip bounds stay finite): fp64
+        # statistics, bucket positions and the merge must not overflow
+        sizes = [5000, 4096 * 2 + 7]
+        tensors, stride = [], 0
+        for n in sizes:
+            tensors.append((stride, stride, n))
+            stride += (n + 63) // 64 * 64
+        gen = torch.Generator(device=DEV)
+        gen.manual_seed(78)
+        theta = torch.randn(stride, generator=gen, device=DEV) * 1e36
+        mom = torch.randn(stride, generator=gen, device=DEV) * 1e33
+        theta_L = torch.empty((2, stride), device=DEV)
+        for i, scale in enumerate([1e34, 1e30]):
+            theta_L[i] = theta - torch.randn(stride, generator=gen, device=DEV) * scale
+        return workloads.StepInputs(theta, mom, theta_L, tensors, [3.0, 1.0], [1, 1], [0, 1], stride)
     raise KeyError(name)
 
 
@@ -119,7 +135,8 @@ def above_hi_inputs():
 
 
 CASES = ["c1", "ragged_k3", "c2_median_fragment", "many_tensors_k20", "absent_k16_const", "sparse_k8",
-         "max_learners_k64", "mean_dominated_k3", "above_hi_mean_dominated_k2", "tiny_values_k3"]
+         "max_learners_k64", "mean_dominated_k3", "above_hi_mean_dominated_k2", "tiny_values_k3",
+         "huge_values_k2"]
 
 
 @pytest.mark.parametrize("name", CASES)
