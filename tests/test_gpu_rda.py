@@ -213,10 +213,12 @@ def test_rda_full_1b_set_sampled_tensors():
         print(f"[rda c3] tensor {t} ({n} params, K = {k}) ok", flush=True)
 
 
-@pytest.mark.parametrize("name", ["mean_dominated_k3", "above_hi_mean_dominated_k2"])
+@pytest.mark.parametrize("name", ["mean_dominated_k3", "above_hi_mean_dominated_k2", "tiny_values_k3",
+                                  "huge_values_k2"])
 def test_rda_norms_from_exact_bucket_counts(name):
-    """Pseudo-gradients whose mean dwarfs their spread, some with elements above hi:
-    the squared norms come from the bucket counts, so they equal sum_c n_c cb_c^2
+    """Pseudo-gradients whose mean dwarfs their spread, some with elements above hi,
+    and values near the bottom and the top of the fp32 range (squares far outside
+    it): the squared norms come from the bucket counts, so they equal sum_c n_c cb_c^2
     with the oracle's counts n_c (codes identical end to end) and the GPU's entries;
     then the oracle's RDA merge on the GPU's codes gives theta and momentum."""
     inp = case_inputs(name)
