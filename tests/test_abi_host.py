@@ -9,6 +9,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import diloco_outer_step_amd as dlc
@@ -55,6 +56,18 @@ def test_fragment_plan_matches_oracle(key, p):
     want = oracle.fragment_plan(numel, p)
     assert got[0] == list(want[0])
     assert got[1] == list(want[1])
+
+
+def test_fragment_plan_random_with_ties():
+    # sizes drawn from few values, so equal sizes and equal loads are common and the
+    # tie rules (equal sizes in index order, equal loads to the lowest fragment) decide
+    rng = np.random.default_rng(5)
+    for case in range(300):
+        n = int(rng.integers(1, 60))
+        pool = rng.integers(1, 5000, int(rng.integers(1, 6)))
+        numel = [int(x) for x in rng.choice(pool, n)]
+        p = int(rng.integers(1, 30))
+        assert dlc.dlc_fragment_plan(numel, p) == oracle.fragment_plan(numel, p), (case, numel, p)
 
 
 def test_fragment_plan_small_cases():
