@@ -77,6 +77,17 @@ def _link(objs, out: str, verbose: bool, sanitize: bool = False) -> str:
     return out
 
 
+def c_program(src: str, out: str, verbose: bool = False) -> str:
+    """Compile a C99 program that calls the C ABI and the HIP runtime (gcc, linked
+    against libdlc.so and libamdhip64 with run paths to both)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    _run(["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__", f"-I{rocm}/include",
+          f"-I{INCLUDE}", src, f"-L{PKG}", "-l:libdlc.so", f"-L{rocm}/lib", "-lamdhip64", "-lm",
+          f"-Wl,-rpath,{PKG}", f"-Wl,-rpath,{rocm}/lib", "-o", out + ".tmp"], verbose)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 def build(verbose: bool = False, hostsan: bool = True) -> str:
     """Compile every HIP source and link libdlc.so (always recompiles); with
     hostsan, also the host-sanitized libdlc_hostsan.so."""
