@@ -16,8 +16,8 @@
 #include <vector>
 
 // Workspace of dlc_quantize_static, for callers that cannot allocate: one copy
-// per device, held until the process ends, shared by every such call on that
-// device (calls that overlap on one device race on it).  No call needs it to
+// per device, held until the process ends, shared by every such call whose
+// stream is on that device (calls that overlap on one device race on it).  No call needs it to
 // start zeroed: every workspace slot is written before it is read.
 static __device__ __align__(256) unsigned char scratch[DLC_STATIC_SCRATCH_BYTES];
 
@@ -607,7 +607,7 @@ size_t quantize_workspace(const dlc_tensor* tensors, int32_t n_tensors, int32_t 
 // The static scratch of dlc_quantize_static (the array is declared at the top of
 // this file).  Host code never uses the array's name as an address: its address
 // on each device comes from hipGetSymbolAddress, looked up once per device (the
-// first call on that device) with the device current, and kept.
+// first call whose stream is on that device) with that device current, and kept.
 constexpr size_t kStaticScratchBytes = DLC_STATIC_SCRATCH_BYTES;
 static_assert(kStaticScratchBytes % 256 == 0, "whole 256-byte units");
 
@@ -616,16 +616,29 @@ std::once_flag g_scratch_once[kMaxDevices];
 void* g_scratch_ptr[kMaxDevices];
 hipError_t g_scratch_err[kMaxDevices];
 
-// This device's address of the scratch array.
-int32_t static_scratch(void** ptr) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "current device");
+// The device a call's work runs on: the stream's (the current device's for the
+// null stream).
+int32_t stream_device(hipStream_t s, int* dev) {
+  const hipError_t e = s == nullptr ? hipGetDevice(dev) : hipStreamGetDevice(s, dev);
+  return e == hipSuccess ? DLC_OK : hip_fail(e, "the stream's device");
+}
+
+// Device dev's address of the scratch array.  The lookup makes dev current and
+// restores the caller's device afterwards.
+int32_t static_scratch(int dev, void** ptr) {
   if (dev < 0 || dev >= kMaxDevices) return fail(DLC_ERR_HIP, "device index beyond the scratch table");
   std::call_once(g_scratch_once[dev], [dev] {
+    int cur = -1;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
     void* p = nullptr;
-    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
-    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur >= 0 && cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
   });
   if (g_scratch_err[dev] != hipSuccess) return hip_fail(g_scratch_err[dev], "static scratch address");
   if (g_scratch_ptr[dev] == nullptr || !aligned256(g_scratch_ptr[dev]))
@@ -738,8 +751,11 @@ int32_t dlc_quantize_static(const float* theta_global, const float* theta_learne
                                        std::to_string(kStaticScratchBytes) +
                                        " of the static scratch: split it into smaller fragments, or pass a "
                                        "workspace to dlc_quantize");
+  int dev = -1;
+  rc = stream_device(static_cast<hipStream_t>(hip_stream), &dev);
+  if (rc != DLC_OK) return rc;
   void* ws = nullptr;
-  rc = static_scratch(&ws);
+  rc = static_scratch(dev, &ws);
   if (rc != DLC_OK) return rc;
   return quantize(theta_global, theta_learners, learner_stride, n_learners, present, tensors, n_tensors, codes,
                   codebook, range, flags, ws, kStaticScratchBytes, hip_stream);

@@ -184,12 +184,14 @@ int32_t dlc_quantize(const float* theta_global, const float* theta_learners,
  *   - A call whose workspace (dlc_workspace_bytes for its present learners)
  *     exceeds DLC_STATIC_SCRATCH_BYTES returns DLC_ERR_WORKSPACE before anything
  *     is enqueued: split it into smaller fragments, or use dlc_quantize.
- *   - Every call on one device shares that device's scratch, which keeps the last
+ *   - The device is the stream's (the current device's for the null stream).
+ *     Every call on one device shares that device's scratch, which keeps the last
  *     call's contents (no call needs it cleared).  Calls that overlap on one
  *     device -- on different streams or threads without ordering -- race on it:
  *     the caller orders them.
- *   - The first call on a device looks up that device's scratch address (the
- *     device must be current); a failure there returns DLC_ERR_HIP.
+ *   - The first call on a device looks up that device's scratch address, making
+ *     the device current for the lookup and restoring the caller's device after
+ *     it; a failure there returns DLC_ERR_HIP.
  * Arguments, flags and errors otherwise as dlc_quantize.
  */
 #define DLC_STATIC_SCRATCH_BYTES 67108864u /* 64 MiB */
