@@ -106,3 +106,58 @@ def test_captured_cycle_replays_the_eager_cycle(mode):
         torch.cuda.synchronize()
         assert torch.equal(th, th_e) and torch.equal(mo, mo_e) and torch.equal(tl, tl_e), rep
         assert torch.equal(cb, cb_e) and torch.equal(rng, rng_e), rep
+
+
+@pytest.mark.parametrize("call", ["rda", "ring"])
+def test_captured_rda_and_ring_replay_the_eager_calls(call):
+    """dlc_rda_outer_step and dlc_ring_outer_step (several kernels each, ranges,
+    codebooks, squared norms or ring messages in between) captured once and
+    replayed: every replay equals the eager call bit for bit."""
+    sizes = [1, 65, 4097, 64 * 300 + 9, 100003]
+    cfg = workloads.custom("graph_" + call, sizes, 4, weights="dirichlet")
+    inp = workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV)
+    k, stride = inp.theta_L.shape
+
+    def buffers():
+        b = dict(th=inp.theta_g.clone(), mo=inp.momentum.clone())
+        if call == "rda":
+            b["codes"], b["cb"], b["rng"] = dlc.outputs_for(k, stride, len(sizes), DEV)
+            b["norms"] = torch.zeros((k, len(sizes)), dtype=torch.float64, device=DEV)
+            need = dlc.dlc_rda_workspace_bytes(k, inp.tensors)
+        else:
+            b["accum"], b["codes"], b["cb"], b["rng"] = dlc.ring_buffers(inp.theta_L, len(sizes))
+            need = dlc.dlc_ring_workspace_bytes(k, inp.tensors)
+        b["ws"] = torch.empty(max(256, need), dtype=torch.uint8, device=DEV)
+        return b
+
+    def run(b):
+        if call == "rda":
+            dlc.dlc_rda_outer_step(b["th"], b["mo"], inp.theta_L, inp.tensors, inp.weights, b["codes"], b["cb"],
+                                   b["rng"], b["norms"], b["ws"])
+        else:
+            dlc.dlc_ring_outer_step(b["th"], b["mo"], inp.theta_L, inp.tensors, b["accum"], b["codes"], b["cb"],
+                                    b["rng"], b["ws"])
+
+    eager = buffers()
+    run(eager)
+    torch.cuda.synchronize()
+    b = buffers()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            run(b)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    keys = ["th", "mo", "cb", "rng"] + (["norms"] if call == "rda" else [])
+    for rep in range(3):
+        b["th"].copy_(inp.theta_g)
+        b["mo"].copy_(inp.momentum)
+        noise = torch.randn(1 << 20, device=DEV).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.isfinite(noise)
+        for key in keys:
+            assert torch.equal(b[key], eager[key]), (rep, key)
