@@ -5,7 +5,9 @@
 //   k_range     per-(learner, tensor) mu, sigma -> {lo, hi, wd, mean} (fp64 -> fp32)
 //   k_encode    Delta -> clip -> bucket -> uint8 code (256-byte runs per wave store) + LDS histogram
 //               of (count, fixed-point position sum) per bucket and learner
-//   k_codebook  per-(learner, tensor, bucket) mean of the clipped values -> fp32
+//   k_hist_reduce, k_codebook
+//               per-(learner, tensor, bucket) mean of the clipped values -> fp32, from the
+//               block histograms summed in slices (one kernel when a tensor has one slice)
 //   k_merge     dequantize K learners through fp64 LDS tables w_hat_i * codebook_i,
 //               sum, Nesterov update of theta and momentum, every byte read once
 //
