@@ -14,7 +14,8 @@ lanes, with and without sending the update back, against fragment-by-fragment
 calls (bit-identical, as in tests/test_gpu_cycle.py); a third of them learners
 on one to three older bases (dlc_quantize_bases, the parity bar above); and the
 sets whose learners are all present the requantizing ring (the per-chunk checks
-of tests/test_gpu_ring.py, with at most a tenth of the chunks diverging).
+of tests/test_gpu_ring.py, with at most a tenth of the chunks diverging, each from
+an adjacent-bucket flip).
 """
 import numpy as np
 import pytest
@@ -26,7 +27,7 @@ import workloads
 from tests import parity
 from tests.test_gpu_cycle import assert_same, run_cycle, run_sequential
 from tests.test_gpu_rda import check_merge_on_gpu_codes, gpu_rda
-from tests.test_gpu_ring import check_against_oracle, gpu_ring
+from tests.test_gpu_ring import check_against_oracle, check_divergence_origins, gpu_ring
 
 pytestmark = pytest.mark.gpu
 
@@ -154,9 +155,11 @@ def test_random_set_ring(seed):
     k = len(inp.present)
     print(f"[random set {seed}, ring] {desc}", flush=True)
     mom = torch.randn(inp.momentum.shape, generator=torch.Generator(device=DEV).manual_seed(seed), device=DEV) * 1e-3
-    th, _ = gpu_ring(inp.theta_g, mom, inp.theta_L, inp.tensors)
+    th, _, codes, _ = gpu_ring(inp.theta_g, mom, inp.theta_L, inp.tensors, messages=True)
     theta0, tl = parity.host(inp.theta_g), parity.host(inp.theta_L)
     orc = oracle.ring_outer_step(theta0, parity.host(mom), tl, inp.theta_L.shape[1], inp.tensors, 0.7, 0.9)
     diverged, chunks = check_against_oracle(parity.host(th), orc, theta0, tl, inp.tensors, k)
-    print(f"[random set {seed}, ring] {diverged} of {chunks} chunks diverged", flush=True)
+    origins = check_divergence_origins(codes, orc, inp.tensors, k, check_against_oracle.diverged)
+    print(f"[random set {seed}, ring] {diverged} of {chunks} chunks diverged, first differing hops {origins}",
+          flush=True)
     assert diverged <= chunks // 10

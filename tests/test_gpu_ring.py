@@ -12,8 +12,9 @@ against the CPU oracle's ring_outer_step.
   requantizes what it received).  The bar: per chunk, either 99.9% of theta
   within 1e-9 + 1e-5 |theta| or the chunk counts as diverged; no more chunks
   diverge than measured on the committed seeds (none up to K = 8, two of 48 at
-  K = 16, one of 24 on the 1B set's sampled tensors); every element within the
-  bucket widths the messages can shift it by; the GPU's g within 5% (RMS) of the
+  K = 16, one of 24 on the 1B set's sampled tensors); every diverged chunk matches
+  the oracle's messages up to a hop whose codes differ by adjacent-bucket flips
+  only; every element within the bucket widths the messages can shift it by; the GPU's g within 5% (RMS) of the
   exact mean's scale from the oracle's g; and every gather message of a chunk
   that has not diverged has the oracle's range within one ulp and, where the
   range is identical, its codes (up to a 1e-3 share of adjacent-bucket flips
@@ -157,6 +158,37 @@ def check_gather_messages(codes, rng, orc, tensors, k, diverged):
     return checked
 
 
+def check_divergence_origins(codes, orc, tensors, k, diverged):
+    """Where each diverged chunk left the oracle's ring.  Every hop's messages
+    survive in the code buffer (sender r writes chunk (r - s) mod K at stage s, a
+    different chunk at every stage), so the chunk's messages can be compared hop by
+    hop: the first one whose codes differ must differ only by adjacent-bucket
+    flips, on at most a 1e-3 share of the chunk -- a code on the other side of a
+    bucket edge that an ulp of difference in a range or a sum moved -- and every
+    earlier hop must match exactly.  Returns the first differing hop per chunk."""
+    codes = host(codes)
+    msg = {(t, s, c): (r, q) for (t, s, r, c, q) in orc["messages"]}
+    first = {}
+    for j, a in sorted(diverged):
+        _, lo, n = tensors[j]
+        chunks = oracle.ring_chunks(n, k)
+        c = next(i for i, (x, y) in enumerate(chunks) if x == a and y > x)
+        b = chunks[c][1]
+        for s in range(k):
+            r, q = msg[(j, s, c)]
+            got = codes[r, lo + a:lo + b].astype(np.int64)
+            want = q["codes"].astype(np.int64)
+            mism = got != want
+            if mism.any():
+                assert np.all(np.abs(got[mism] - want[mism]) == 1), f"tensor {j} chunk [{a}, {b}) hop {s}"
+                assert mism.mean() <= 1e-3, f"tensor {j} chunk [{a}, {b}) hop {s}: {int(mism.sum())} codes differ"
+                first[(j, a)] = (s, int(mism.sum()))
+                break
+        else:
+            raise AssertionError(f"tensor {j} chunk [{a}, {b}) diverged with every message's codes equal")
+    return first
+
+
 # diverged chunks measured on these seeds with the current kernels: none up to
 # K = 8, two of 48 at K = 16
 MAX_DIVERGED = {2: 0, 4: 0, 8: 0, 16: 2}
@@ -176,6 +208,8 @@ def test_gaussian_against_oracle(k):
     diverged, chunks = check_against_oracle(host(th), orc, host(theta), host(theta_L), tensors, k)
     print(f"[ring K = {k}] {diverged} of {chunks} chunks diverged", flush=True)
     assert diverged <= MAX_DIVERGED[k], f"{diverged} of {chunks} chunks diverged"
+    origins = check_divergence_origins(codes, orc, tensors, k, check_against_oracle.diverged)
+    print(f"[ring K = {k}] first differing hop and codes per diverged chunk: {origins}", flush=True)
     checked = check_gather_messages(codes, rng, orc, tensors, k, check_against_oracle.diverged)
     assert checked == chunks - diverged
 
