@@ -223,7 +223,7 @@ def test_ring_full_1b_set_sampled_tensors():
     inp = workloads.fragment_inputs(cfg, list(range(len(cfg.tensors))), DEV)
     k = inp.theta_L.shape[0]
     theta0, mom0 = inp.theta_g.clone(), inp.momentum.clone()
-    th, mo = gpu_ring(inp.theta_g, inp.momentum, inp.theta_L, inp.tensors)
+    th, mo, codes, _ = gpu_ring(inp.theta_g, inp.momentum, inp.theta_L, inp.tensors, messages=True)
     sizes = sorted((n, t) for t, (_, _, n) in enumerate(inp.tensors))
     # the smallest tensor, the largest below 2M and the largest below 5M elements (2048, 512 x 2048, 2048^2)
     picks = sorted({sizes[0][1], max((n, t) for n, t in sizes if n <= 2_000_000)[1],
@@ -241,6 +241,9 @@ def test_ring_full_1b_set_sampled_tensors():
         th_gpu[o2:o2 + n] = host(th[o:o + n])
     orc = oracle.ring_outer_step(th0, mo0, tl, stride, sub, LR, BETA)
     diverged, chunks = check_against_oracle(th_gpu, orc, th0, tl, sub, k)
+    # the picked tensors where the GPU's code buffer holds them
+    at_gpu = [(inp.tensors[t][0], inp.tensors[t][1], n) for (_, _, n), t in zip(sub, picks)]
+    origins = check_divergence_origins(codes, orc, at_gpu, k, check_against_oracle.diverged)
     print(f"[ring c3] tensors {picks} ({[n for _, _, n in sub]} params, K = {k}): "
-          f"{diverged} of {chunks} chunks diverged", flush=True)
+          f"{diverged} of {chunks} chunks diverged, first differing hops {origins}", flush=True)
     assert diverged <= 1  # measured: one of 24
