@@ -341,13 +341,14 @@ def broadcast(theta_g, theta_L, tensors, rows=None):
 
 
 def outer_cycle(theta_g, momentum, theta_L, learner_stride, tensors, fragment_first, weights,
-                lr=0.7, beta=0.9, send_back=False):
+                lr=0.7, beta=0.9, send_back=False, rule="mean"):
     """One outer step over every fragment in id order (Decoupled DiLoCo digest,
     "architecture" item 4).  Fragment f owns tensors[fragment_first[f]:
     fragment_first[f + 1]] and merges with weights[f] (0 = learner absent for
-    that fragment).  With send_back, the fragment's updated tensors are copied to
-    every learner right after its merge.  Returns dict(theta, momentum, theta_L,
-    steps={f: outer_step result})."""
+    that fragment), by the weighted mean or, with rule "rda", by Radial-
+    Directional Averaging (the digest's merge, see rda_merge).  With send_back,
+    the fragment's updated tensors are copied to every learner right after its
+    merge.  Returns dict(theta, momentum, theta_L, steps={f: outer_step result})."""
     th = np.array(theta_g, dtype=np.float32, copy=True)
     mom = np.array(momentum, dtype=np.float32, copy=True)
     tl = np.array(theta_L, dtype=np.float32, copy=True)
@@ -357,7 +358,7 @@ def outer_cycle(theta_g, momentum, theta_L, learner_stride, tensors, fragment_fi
         if not sel:
             continue
         w = list(weights[f])
-        res = outer_step(th, mom, tl, learner_stride, sel, w, [1 if x > 0 else 0 for x in w], lr, beta)
+        res = outer_step(th, mom, tl, learner_stride, sel, w, [1 if x > 0 else 0 for x in w], lr, beta, rule=rule)
         th, mom = res["theta"], res["momentum"]
         steps[f] = res
         if send_back:

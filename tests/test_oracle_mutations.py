@@ -91,6 +91,13 @@ def _rda_exact_zero_test(codes_per_learner, codebook_per_learner, w_hat):
     return r * d / dn if dn > 0.0 else np.zeros_like(d)
 
 
+_OUTER_STEP = core.outer_step
+
+
+def _step_ignoring_rule(*args, rule="mean", **kwargs):
+    return _OUTER_STEP(*args, **kwargs)
+
+
 def _ring_wrong_direction(rank, hop, k):
     return (rank + hop) % k
 
@@ -160,6 +167,8 @@ MUTATIONS = {
                         lambda: pins.test_rda_orthogonal_halves_closed_form(3.0, 1.0)]),
     "rda_null_direction_tested_exactly": (lambda mp: _patch(mp, "rda_merge", _rda_exact_zero_test),
                                           [lambda: pins.test_rda_balanced_constant_learners_give_zero(2)]),
+    "cycle_ignores_the_merge_rule": (lambda mp: _patch(mp, "outer_step", _step_ignoring_rule),
+                                     [pins.test_rda_cycle_is_not_the_mean_cycle]),
     "rda_unweighted_norm": (lambda mp: _patch(mp, "rda_merge", _rda_unweighted_norm),
                             [lambda: pins.test_rda_norm_is_the_weighted_mean_norm(0)]),
     "ring_chunks_travel_the_wrong_way": (lambda mp: _patch(mp, "ring_sent_chunk", _ring_wrong_direction),

@@ -520,6 +520,36 @@ def test_cycle_result_does_not_depend_on_fragment_order():
         np.testing.assert_array_equal(a[key], b[key])
 
 
+def test_rda_cycle_is_its_fragments_rda_steps_stitched():
+    # Without send-back nothing couples disjoint fragments: the cycle equals each
+    # fragment's own RDA step from the initial state, stitched together.
+    theta, mom, tl, stride, tensors = _cycle_case(4)
+    w = [[1.0, 2.0, 0.5], [0.0, 1.0, 3.0], [2.0, 2.0, 2.0]]
+    first = [0, 2, 3, 5]
+    cyc = oracle.outer_cycle(theta, mom, tl, stride, tensors, first, w, rule="rda")
+    th, mo = theta.copy(), mom.copy()
+    for f in range(3):
+        sel = tensors[first[f]:first[f + 1]]
+        one = oracle.outer_step(theta, mom, tl, stride, sel, w[f], [1 if x > 0 else 0 for x in w[f]], rule="rda")
+        for o, _, n in sel:
+            th[o:o + n] = one["theta"][o:o + n]
+            mo[o:o + n] = one["momentum"][o:o + n]
+    np.testing.assert_array_equal(cyc["theta"], th)
+    np.testing.assert_array_equal(cyc["momentum"], mo)
+
+
+def test_rda_cycle_is_not_the_mean_cycle():
+    # learners of very different norms: averaging directions and norms separately
+    # moves theta differently from the weighted mean
+    theta, mom, tl, stride, tensors = _cycle_case(5)
+    tl[2] = theta - 10.0 * (theta - tl[2])
+    w = [[1.0, 1.0, 1.0], [1.0, 2.0, 1.0]]
+    first = [0, 3, 5]
+    a = oracle.outer_cycle(theta, mom, tl, stride, tensors, first, w, rule="rda")
+    b = oracle.outer_cycle(theta, mom, tl, stride, tensors, first, w)
+    assert np.max(np.abs(a["theta"] - b["theta"])) > 1e-4
+
+
 def test_after_sending_back_the_next_cycle_is_a_pure_momentum_step():
     # Once every learner holds the merged theta, each pseudo-gradient is exactly
     # zero: every tensor is degenerate (codes 0, codebook = mean = 0), g = 0, and
