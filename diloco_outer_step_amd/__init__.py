@@ -46,7 +46,8 @@ EXPORTED = (
     "dlc_fragment_plan", "dlc_workspace_bytes", "dlc_quantize_range", "dlc_quantize_encode",
     "dlc_quantize", "dlc_quantize_static", "dlc_quantize_bases", "dlc_merge_outer_step", "dlc_merge_weights", "dlc_broadcast",
     "dlc_cycle_workspace_bytes", "dlc_outer_cycle", "dlc_outer_cycle_lanes", "dlc_ring_workspace_bytes", "dlc_ring_outer_step",
-    "dlc_rda_workspace_bytes", "dlc_rda_outer_step", "dlc_last_error", "dlc_version",
+    "dlc_rda_workspace_bytes", "dlc_rda_outer_step", "dlc_cycle_rda_workspace_bytes", "dlc_outer_cycle_rda",
+    "dlc_last_error", "dlc_version",
 )
 
 
@@ -93,6 +94,9 @@ def _load() -> ctypes.CDLL:
                             u32, vp, sz, vp, vp],
         "dlc_outer_cycle_lanes": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, ctypes.c_double,
                                   ctypes.c_double, u32, vp, sz, vp, i32],
+        "dlc_cycle_rda_workspace_bytes": [i32, tp, vp, i32, ctypes.POINTER(sz)],
+        "dlc_outer_cycle_rda": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, vp, ctypes.c_double,
+                                ctypes.c_double, u32, vp, sz, vp, i32],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -472,7 +476,8 @@ def group_by_fragment(tensors, fragment_of, n_fragments):
     return [tensors[t] for t in order], first, order
 
 
-def _cycle_checks(theta_g, momentum, theta_L, tensors, nf, weights, codes, codebook, range_out, workspace):
+def _cycle_checks(theta_g, momentum, theta_L, tensors, nf, weights, codes, codebook, range_out, workspace,
+                  sq_norms=None):
     """Buffer checks of a fragment cycle -> (weights as a C array, K, learner_stride)."""
     c = _Checks()
     k, stride = c.learners(theta_L, tensors)
@@ -482,7 +487,7 @@ def _cycle_checks(theta_g, momentum, theta_L, tensors, nf, weights, codes, codeb
         if len(row) != k:
             raise ValueError(f"weights[{f}] holds {len(row)} values for {k} learners")
     c.global_(tensors, theta_g=theta_g, momentum=momentum)
-    c.outputs(k, len(tensors), codes, stride, codebook, range_out)
+    c.outputs(k, len(tensors), codes, stride, codebook, range_out, sq_norms)
     c.workspace(workspace)
     c.done()
     return (ctypes.c_double * (nf * k))(*[float(x) for row in weights for x in row]), k, stride
@@ -529,6 +534,34 @@ def dlc_outer_cycle_lanes(theta_g, momentum, theta_L, tensors, fragment_first, w
                                       _ptr(range_out), float(lr), float(beta), DLC_BROADCAST if broadcast else 0,
                                       _ptr(workspace), workspace.numel(), ctypes.cast(ss, ctypes.c_void_p),
                                       len(streams)))
+
+
+def dlc_cycle_rda_workspace_bytes(n_learners: int, tensors, fragment_first) -> int:
+    arr, _ = _tensors(tensors)
+    _fb, fp = _fragments(fragment_first)
+    out = ctypes.c_size_t(0)
+    _check(_lib.dlc_cycle_rda_workspace_bytes(int(n_learners), arr, fp, len(fragment_first) - 1, ctypes.byref(out)))
+    return out.value
+
+
+def dlc_outer_cycle_rda(theta_g, momentum, theta_L, tensors, fragment_first, weights, codes, codebook, range_out,
+                        sq_norms, workspace, streams, lr=0.7, beta=0.9, broadcast=False):
+    """The fragment cycle on the given streams with every fragment merged by
+    Radial-Directional Averaging; sq_norms is fp64 [n_learners][n_tensors]
+    (workspace of len(streams) times dlc_cycle_rda_workspace_bytes)."""
+    if sq_norms is None:
+        raise ValueError("sq_norms is required")
+    nf = len(fragment_first) - 1
+    w, k, stride = _cycle_checks(theta_g, momentum, theta_L, tensors, nf, weights, codes, codebook, range_out,
+                                 workspace, sq_norms)
+    arr, _ = _tensors(tensors)
+    _fb, fp = _fragments(fragment_first)
+    ss = (ctypes.c_void_p * max(1, len(streams)))(*[_stream(s).value for s in streams])
+    _check(_lib.dlc_outer_cycle_rda(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), stride, k,
+                                    ctypes.cast(w, ctypes.c_void_p), arr, fp, nf, _ptr(codes), _ptr(codebook),
+                                    _ptr(range_out), _ptr(sq_norms), float(lr), float(beta),
+                                    DLC_BROADCAST if broadcast else 0, _ptr(workspace), workspace.numel(),
+                                    ctypes.cast(ss, ctypes.c_void_p), len(streams)))
 
 
 def outputs_for(n_learners: int, learner_stride: int, n_tensors: int, device="cuda"):

@@ -440,6 +440,23 @@ RdaWorkspace rda_workspace(int32_t n_learners, const dlc_tensor* tensors, int32_
   return w;
 }
 
+// One fragment of a cycle merged by Radial-Directional Averaging, in its lane's
+// share of the workspace: the quantize layout, one fp64 direction sum per
+// direction block, then the coefficient table of every row of the cycle's tables
+// ([rows_total][n_learners], the rows k_rda_coef and the merge index).
+RdaWorkspace fragment_rda_workspace(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                                    int32_t rows_total) {
+  RdaWorkspace w;
+  const Partition ps = stats_partition(tensors, n_tensors);
+  const Partition pe = encode_partition(tensors, n_tensors);
+  const Partition pm = direction_partition(tensors, n_tensors);
+  w.quant = workspace_layout(ps.n_slots, pe.n_slots, n_tensors, n_learners).total;
+  w.dir_part = w.quant;
+  w.coef = w.dir_part + round256((size_t)pm.n_slots * sizeof(double));
+  w.total = w.coef + round256((size_t)rows_total * (size_t)n_learners * sizeof(double));
+  return w;
+}
+
 int32_t check_fragments(const dlc_tensor* tensors, const int32_t* fragment_first, int32_t n_fragments) {
   if (!tensors || !fragment_first) return fail(DLC_ERR_INVALID_ARGUMENT, "tensors and fragment_first must not be NULL");
   if (n_fragments < 1) return fail(DLC_ERR_INVALID_ARGUMENT, "n_fragments must be >= 1");
@@ -470,16 +487,20 @@ hipError_t order_after(hipStream_t from, hipStream_t to) {
 // (and broadcasts) on merge_stream, each merge after its fragment's quantization
 // through an event.  n_lanes >= 1: the non-empty fragments take the lanes in turn,
 // each lane with its own stream and its own equal share of the workspace, and a
-// fragment's quantize, merge and broadcast all run on its lane.
+// fragment's quantize, merge and broadcast all run on its lane.  sq_norms set:
+// every fragment merges by Radial-Directional Averaging (its direction pass and
+// coefficients on the merge's stream, before the merge), with the squared norms
+// written to sq_norms [n_learners][rows].
 int32_t outer_cycle(float* theta_global, float* momentum, float* theta_learners, int64_t learner_stride,
                     int32_t n_learners, const double* weights, const dlc_tensor* tensors,
                     const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
                     float* range, double lr, double beta, bool broadcast, void* workspace, size_t workspace_bytes,
                     hipStream_t quantize_stream, hipStream_t merge_stream, const hipStream_t* lane_streams,
-                    int32_t n_lanes) {
+                    int32_t n_lanes, double* sq_norms = nullptr) {
   if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
-  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
-    return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
+  if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook) || (sq_norms && !aligned256(sq_norms)))
+    return fail(DLC_ERR_ALIGNMENT, "range, codes, codebook and sq_norms must be 256-byte aligned");
+  const bool rda = sq_norms != nullptr;
   int32_t rc = check_fragments(tensors, fragment_first, n_fragments);
   if (rc != DLC_OK) return rc;
   const int32_t n_tensors = fragment_first[n_fragments];
@@ -492,6 +513,7 @@ int32_t outer_cycle(float* theta_global, float* momentum, float* theta_learners,
   // quantize setup (workspace size) for every non-empty fragment.
   std::vector<dlc::MergeArgs> margs(n_fragments);
   std::vector<Common> qc(n_fragments);
+  std::vector<RdaWorkspace> frw(n_fragments);
   std::vector<int32_t> lane(n_fragments, 0);
   std::vector<uint8_t> present(n_learners);
   int32_t busy = 0;
@@ -504,13 +526,22 @@ int32_t outer_cycle(float* theta_global, float* momentum, float* theta_learners,
     if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
     for (int32_t i = 0; i < n_learners; ++i) present[i] = w[i] > 0.0 ? 1 : 0;
     void* lane_ws = workspace == nullptr ? nullptr : static_cast<char*>(workspace) + (size_t)lane[f] * share;
+    size_t quant_bytes = share;
+    if (rda) {
+      frw[f] = fragment_rda_workspace(n_learners, tensors + fragment_first[f], n, n_tensors);
+      if (lane_ws != nullptr && share < frw[f].total)
+        return fail(DLC_ERR_WORKSPACE, "fragment " + std::to_string(f) + ": workspace too small: need " +
+                                           std::to_string(frw[f].total) + " bytes per lane");
+      quant_bytes = frw[f].quant;
+    }
     rc = setup_quant(qc[f], theta_global, theta_learners, learner_stride, n_learners, present.data(),
-                     tensors + fragment_first[f], n, lane_ws, share, lanes ? lane_streams[lane[f]] : quantize_stream,
-                     fragment_first[f], n_tensors);
+                     tensors + fragment_first[f], n, lane_ws, quant_bytes,
+                     lanes ? lane_streams[lane[f]] : quantize_stream, fragment_first[f], n_tensors);
     if (rc != DLC_OK) return fail(rc, "fragment " + std::to_string(f) + ": " + g_last_error);
     qc[f].args.range = reinterpret_cast<float4*>(range);
     qc[f].args.codes = codes;
     qc[f].args.codebook = codebook;
+    qc[f].args.norm2 = sq_norms;
   }
   hipError_t e = hipSuccess;
   // the other lanes start after the work already on the first lane's stream (this
@@ -532,7 +563,28 @@ int32_t outer_cycle(float* theta_global, float* momentum, float* theta_learners,
       e = order_after(quantize_stream, merge_stream);
       if (e != hipSuccess) return hip_fail(e, "cycle event");
     }
-    rc = run_merge(margs[f], tensors + fragment_first[f], n, fragment_first[f], n_tensors, ms);
+    if (rda) {
+      // direction norms, then the coefficients, then the merge with them (all on ms)
+      char* ws = static_cast<char*>(workspace) + (size_t)lane[f] * share;
+      dlc::MergeArgs ma = margs[f];
+      ma.norm2 = sq_norms;
+      ma.dir_part = reinterpret_cast<double*>(ws + frw[f].dir_part);
+      Partition pm = direction_partition(tensors + fragment_first[f], n);
+      set_rows(pm, fragment_first[f], n_tensors);
+      for (const dlc::LaunchGeom& g : pm.launches) {
+        e = dlc::launch_rda_direction(ma, g, ms);
+        if (e != hipSuccess) return hip_fail(e, "direction kernel launch");
+      }
+      ma.coef = reinterpret_cast<double*>(ws + frw[f].coef);
+      for (const dlc::LaunchGeom& g : pm.launches) {
+        e = dlc::launch_rda_coef(ma, g, ms);
+        if (e != hipSuccess) return hip_fail(e, "coefficient kernel launch");
+      }
+      ma.dir_part = nullptr;
+      rc = run_merge(ma, tensors + fragment_first[f], n, fragment_first[f], n_tensors, ms);
+    } else {
+      rc = run_merge(margs[f], tensors + fragment_first[f], n, fragment_first[f], n_tensors, ms);
+    }
     if (rc == DLC_OK && broadcast)
       rc = run_broadcast(theta_global, theta_learners, learner_stride, n_learners, nullptr,
                          tensors + fragment_first[f], n, ms);
@@ -879,6 +931,43 @@ int32_t dlc_outer_cycle_lanes(float* theta_global, float* momentum, float* theta
   return outer_cycle(theta_global, momentum, theta_learners, learner_stride, n_learners, weights, tensors,
                      fragment_first, n_fragments, codes, codebook, range, lr, beta, (flags & DLC_BROADCAST) != 0,
                      workspace, workspace_bytes, lane_streams[0], lane_streams[0], lane_streams, n_lanes);
+}
+
+int32_t dlc_cycle_rda_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, const int32_t* fragment_first,
+                                      int32_t n_fragments, size_t* bytes) {
+  if (!bytes) return fail(DLC_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  if (n_learners < 1 || n_learners > DLC_MAX_LEARNERS)
+    return fail(DLC_ERR_INVALID_ARGUMENT, "n_learners must be in [1, 64]");
+  int32_t rc = check_fragments(tensors, fragment_first, n_fragments);
+  if (rc != DLC_OK) return rc;
+  const int32_t rows = fragment_first[n_fragments];
+  size_t most = 0;
+  for (int32_t f = 0; f < n_fragments; ++f) {
+    const int32_t n = fragment_first[f + 1] - fragment_first[f];
+    if (n == 0) continue;
+    const dlc_tensor* t = tensors + fragment_first[f];
+    rc = check_tensors(t, n, 0, false);
+    if (rc != DLC_OK) return rc;
+    most = std::max(most, fragment_rda_workspace(n_learners, t, n, rows).total);
+  }
+  *bytes = most;
+  return ok();
+}
+
+int32_t dlc_outer_cycle_rda(float* theta_global, float* momentum, float* theta_learners, int64_t learner_stride,
+                            int32_t n_learners, const double* weights, const dlc_tensor* tensors,
+                            const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
+                            float* range, double* sq_norms, double lr, double beta, uint32_t flags, void* workspace,
+                            size_t workspace_bytes, void* const* streams, int32_t n_lanes) {
+  if ((flags & ~DLC_BROADCAST) != 0) return fail(DLC_ERR_INVALID_ARGUMENT, "unknown flag");
+  if (n_lanes < 1 || n_lanes > DLC_MAX_LANES) return fail(DLC_ERR_INVALID_ARGUMENT, "n_lanes must be in [1, 8]");
+  if (!streams) return fail(DLC_ERR_INVALID_ARGUMENT, "streams is NULL");
+  if (!sq_norms) return fail(DLC_ERR_INVALID_ARGUMENT, "sq_norms is NULL");
+  hipStream_t lane_streams[DLC_MAX_LANES];
+  for (int32_t l = 0; l < n_lanes; ++l) lane_streams[l] = static_cast<hipStream_t>(streams[l]);
+  return outer_cycle(theta_global, momentum, theta_learners, learner_stride, n_learners, weights, tensors,
+                     fragment_first, n_fragments, codes, codebook, range, lr, beta, (flags & DLC_BROADCAST) != 0,
+                     workspace, workspace_bytes, lane_streams[0], lane_streams[0], lane_streams, n_lanes, sq_norms);
 }
 
 int32_t dlc_merge_weights(int32_t n_learners, const double* tokens, const double* arrival, int32_t quorum,

@@ -326,6 +326,33 @@ int32_t dlc_outer_cycle_lanes(float* theta_global, float* momentum, float* theta
                               size_t workspace_bytes, void* const* streams, int32_t n_lanes);
 
 /*
+ * dlc_outer_cycle_rda -- the cycle of dlc_outer_cycle_lanes with every fragment
+ * merged by Radial-Directional Averaging (Decoupled DiLoCo digest,
+ * "architecture": the syncer merges one fragment at a time, averaging the outer
+ * gradients' directions and norms separately).  Fragment f's step is exactly
+ * dlc_rda_outer_step over its tensors with weights[f]; the results equal those
+ * calls made fragment by fragment on one stream, bit for bit.
+ *   sq_norms    device fp64 [n_learners][n_tensors], written for every present
+ *               (learner, tensor) pair: the squared norm of the dequantized
+ *               pseudo-gradient, as dlc_rda_outer_step
+ *   workspace   >= n_lanes * dlc_cycle_rda_workspace_bytes(...) bytes, split into
+ *               n_lanes equal shares (each rounded down to 256 bytes)
+ *   flags       0 or DLC_BROADCAST
+ * Other arguments, streams, ordering and errors as dlc_outer_cycle_lanes.
+ */
+int32_t dlc_outer_cycle_rda(float* theta_global, float* momentum, float* theta_learners, int64_t learner_stride,
+                            int32_t n_learners, const double* weights, const dlc_tensor* tensors,
+                            const int32_t* fragment_first, int32_t n_fragments, uint8_t* codes, float* codebook,
+                            float* range, double* sq_norms, double lr, double beta, uint32_t flags, void* workspace,
+                            size_t workspace_bytes, void* const* streams, int32_t n_lanes);
+
+/* Workspace bytes of one lane of dlc_outer_cycle_rda: the largest fragment's
+ * quantize workspace, its direction sums and a coefficient table of
+ * n_learners * n_tensors doubles. */
+int32_t dlc_cycle_rda_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, const int32_t* fragment_first,
+                                      int32_t n_fragments, size_t* bytes);
+
+/*
  * dlc_merge_weights -- which learners a fragment's merge takes, and their weights
  * (Decoupled DiLoCo digest, "fault tolerance" items 1-3: merge once a minimum
  * quorum has arrived, wait a little longer while the window has slack, weight

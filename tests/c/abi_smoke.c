@@ -80,6 +80,9 @@ int main(void) {
   const int32_t first[5] = {0, 2, 2, 5, 5};
   check(dlc_cycle_workspace_bytes(4, ragged, first, 4, &bytes) == DLC_OK && bytes > 0,
         "cycle workspace with empty fragments");
+  size_t rda_bytes = 0;
+  check(dlc_cycle_rda_workspace_bytes(4, ragged, first, 4, &rda_bytes) == DLC_OK && rda_bytes > bytes,
+        "RDA cycle workspace exceeds the cycle's");
   const int32_t bad_first[3] = {0, 3, 2};
   check(dlc_cycle_workspace_bytes(4, ragged, bad_first, 2, &bytes) == DLC_ERR_INVALID_ARGUMENT,
         "decreasing fragment_first rejected");
@@ -145,6 +148,18 @@ int main(void) {
   check(dlc_outer_cycle_lanes(F, F, F, 1 << 20, 2, ones, ragged, cycle_first, 3, U, F, F, 0.7, 0.9, 0, W,
                               (size_t)1 << 40, streams, 9) == DLC_ERR_INVALID_ARGUMENT,
         "nine lanes rejected");
+  check(dlc_outer_cycle_rda(F, F, F, 1 << 20, 2, ones, ragged, cycle_first, 3, U, F, F, NULL, 0.7, 0.9, 0, W,
+                            (size_t)1 << 40, streams, 1) == DLC_ERR_INVALID_ARGUMENT,
+        "RDA cycle: NULL sq_norms rejected");
+  check(dlc_outer_cycle_rda(F, F, F, 1 << 20, 2, cycle_w, ragged, cycle_first, 3, U, F, F, (double*)F, 0.7, 0.9, 0,
+                            W, (size_t)1 << 40, streams, 2) == DLC_ERR_NO_QUORUM,
+        "RDA cycle: a fragment short of its quorum enqueues nothing");
+  check(dlc_outer_cycle_rda(F, F, F, 1 << 20, 2, ones, ragged, cycle_first, 3, U, F, F, (double*)F, 0.7, 0.9, 0, W,
+                            512, streams, 2) == DLC_ERR_WORKSPACE,
+        "RDA cycle: small lane shares rejected");
+  check(dlc_outer_cycle_rda(F, F, F, 1 << 20, 2, ones, ragged, cycle_first, 3, U, F, F, (double*)F, 0.7, 0.9,
+                            DLC_TWO_LANES, W, (size_t)1 << 40, streams, 2) == DLC_ERR_INVALID_ARGUMENT,
+        "RDA cycle: unknown flag");
   check(dlc_ring_outer_step(F, F, F, 1 << 20, 7, ragged, 5, 0.7, 0.9, F, U, F, F, W, 256, NULL) ==
             DLC_ERR_WORKSPACE,
         "ring: small workspace rejected");

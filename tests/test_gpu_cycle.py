@@ -189,3 +189,93 @@ def test_c2_cycle_with_send_back_equals_sequential():
     assert_same(c, b, weights, grouped, first)
     d = run_cycle(*args, broadcast=True, two_streams=False, lanes=[None, torch.cuda.Stream(), torch.cuda.Stream()])
     assert_same(d, b, weights, grouped, first)
+
+
+def run_cycle_rda(theta, mom, theta_L, grouped, first, weights, broadcast, lanes):
+    """dlc_outer_cycle_rda on the given lanes (None = the current stream)."""
+    k, stride = theta_L.shape
+    theta, mom, theta_L = theta.clone(), mom.clone(), theta_L.clone()
+    codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), DEV)
+    norms = torch.zeros((k, len(grouped)), dtype=torch.float64, device=DEV)
+    need = (dlc.dlc_cycle_rda_workspace_bytes(k, grouped, first) + 256) * len(lanes)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    qs = torch.cuda.current_stream()
+    dlc.dlc_outer_cycle_rda(theta, mom, theta_L, grouped, first, weights, codes, cb, rng, norms, ws,
+                            [qs if s is None else s for s in lanes], broadcast=broadcast)
+    torch.cuda.synchronize()
+    return dict(theta=theta, momentum=mom, theta_L=theta_L, codes=codes, codebook=cb, range=rng, sq_norms=norms)
+
+
+def run_sequential_rda(theta, mom, theta_L, grouped, first, weights, broadcast):
+    """dlc_rda_outer_step fragment by fragment on one stream."""
+    k, stride = theta_L.shape
+    theta, mom, theta_L = theta.clone(), mom.clone(), theta_L.clone()
+    codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), DEV)
+    norms = torch.zeros((k, len(grouped)), dtype=torch.float64, device=DEV)
+    for f in range(len(first) - 1):
+        sel = grouped[first[f]:first[f + 1]]
+        if not sel:
+            continue
+        _, cbf, rf = dlc.outputs_for(k, 64, len(sel), DEV)
+        nf = torch.zeros((k, len(sel)), dtype=torch.float64, device=DEV)
+        ws = torch.empty(max(256, dlc.dlc_rda_workspace_bytes(k, sel)), dtype=torch.uint8, device=DEV)
+        dlc.dlc_rda_outer_step(theta, mom, theta_L, sel, weights[f], codes, cbf, rf, nf, ws)
+        if broadcast:
+            dlc.dlc_broadcast(theta, theta_L, sel)
+        torch.cuda.synchronize()
+        for i in range(k):
+            if weights[f][i] > 0:
+                cb[i, first[f]:first[f + 1]] = cbf[i]
+                rng[i, first[f]:first[f + 1]] = rf[i]
+                norms[i, first[f]:first[f + 1]] = nf[i]
+    return dict(theta=theta, momentum=mom, theta_L=theta_L, codes=codes, codebook=cb, range=rng, sq_norms=norms)
+
+
+@pytest.mark.parametrize("n_lanes", [1, 3, 4])
+@pytest.mark.parametrize("broadcast", [False, True])
+def test_rda_cycle_equals_fragment_by_fragment(n_lanes, broadcast):
+    """dlc_outer_cycle_rda against dlc_rda_outer_step called fragment by fragment:
+    the same kernels on the same partitions, so every output is bit-identical,
+    the squared norms included."""
+    sizes = RAGGED + [4096] * 12 + [64 * 3000 + 7] * 3 + [1 << 18]
+    args = cycle_inputs(11, 5, sizes, 8)
+    lanes = [None] + [torch.cuda.Stream() for _ in range(n_lanes - 1)]
+    a = run_cycle_rda(*args, broadcast=broadcast, lanes=lanes)
+    b = run_sequential_rda(*args, broadcast=broadcast)
+    weights, grouped, first = args[5], args[3], args[4]
+    assert_same(a, b, weights, grouped, first)
+    for f in range(len(first) - 1):
+        for i, w in enumerate(weights[f]):
+            if w > 0:
+                assert torch.equal(a["sq_norms"][i, first[f]:first[f + 1]], b["sq_norms"][i, first[f]:first[f + 1]])
+
+
+def test_rda_cycle_against_oracle():
+    """The RDA cycle with send-back, an empty fragment and absent learners against
+    the oracle's cycle with the RDA rule: each fragment's quantization at the
+    parity bar, and theta and momentum within the step tolerance wherever no code
+    flipped."""
+    sizes = [5000, 4096 * 3 + 1, 777, 64 * 100, 9000, 20000]
+    k = 4
+    theta, mom, theta_L, grouped, first, weights = cycle_inputs(13, k, sizes, 4)
+    first = [0, 2, 2, 4, 6]  # fragment 1 empty
+    stride = theta_L.shape[1]
+    gpu = run_cycle_rda(theta, mom, theta_L, grouped, first, weights, broadcast=True,
+                        lanes=[None, torch.cuda.Stream()])
+    orc = oracle.outer_cycle(theta.cpu().numpy(), mom.cpu().numpy(), theta_L.cpu().numpy(), stride, grouped, first,
+                             weights, send_back=True, rule="rda")
+    th_g, th_o = parity.host(gpu["theta"]).astype(np.float64), orc["theta"].astype(np.float64)
+    for f, res in orc["steps"].items():
+        sel = grouped[first[f]:first[f + 1]]
+        view = workloads.StepInputs(theta, mom, theta_L, sel, weights[f], [1 if w > 0 else 0 for w in weights[f]],
+                                    list(range(len(sel))), stride)
+        g = dict(codes=gpu["codes"], codebook=gpu["codebook"][:, first[f]:first[f + 1]],
+                 range=gpu["range"][:, first[f]:first[f + 1]], theta=gpu["theta"], momentum=gpu["momentum"])
+        rep = parity.compare(g, res, view, pinned=False, state=False)
+        if rep["flips"] == 0:
+            for o, _, n in sel:
+                d = np.abs(th_g[o:o + n] - th_o[o:o + n])
+                assert np.all(d <= parity.ATOL + parity.RTOL * np.abs(th_o[o:o + n])), (f, o)
+    for _, lo, n in grouped:
+        for i in range(k):
+            assert torch.equal(gpu["theta_L"][i, lo:lo + n], gpu["theta"][lo:lo + n])

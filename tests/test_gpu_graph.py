@@ -53,13 +53,15 @@ def test_captured_step_replays_the_eager_step():
         assert torch.equal(th, th_e) and torch.equal(mo, mo_e), rep
 
 
-@pytest.mark.parametrize("mode", ["two_streams", "two_lanes", "three_lanes", "four_lanes"])
+@pytest.mark.parametrize("mode", ["two_streams", "two_lanes", "three_lanes", "four_lanes", "rda_four_lanes"])
 def test_captured_cycle_replays_the_eager_cycle(mode):
     """A whole fragment cycle on two streams (the second joins the capture through
-    the cycle's own events), on two lanes, and on three and four lanes through
-    dlc_outer_cycle_lanes, captured once and replayed."""
+    the cycle's own events), on two lanes, on three and four lanes through
+    dlc_outer_cycle_lanes, and on four lanes merged by Radial-Directional
+    Averaging (dlc_outer_cycle_rda), captured once and replayed."""
     two_lanes = mode == "two_lanes"
-    n_lanes = {"three_lanes": 3, "four_lanes": 4}.get(mode, 0)
+    rda = mode.startswith("rda")
+    n_lanes = {"three_lanes": 3, "four_lanes": 4, "rda_four_lanes": 4}.get(mode, 0)
     sizes = [4096] * 6 + [64 * 1000 + 5] * 3 + [1 << 17, 777]
     cfg = workloads.custom("graph_cycle", sizes, 4)
     inp = workloads.fragment_inputs(cfg, list(range(len(sizes))), DEV)
@@ -67,17 +69,24 @@ def test_captured_cycle_replays_the_eager_cycle(mode):
     frag, _ = dlc.dlc_fragment_plan(sizes, 5)
     grouped, first, _ = dlc.group_by_fragment(inp.tensors, frag, 5)
     weights = [list(inp.weights)] * 5
-    need = (dlc.dlc_cycle_workspace_bytes(k, grouped, first) + 256) * 4
+    need = (max(dlc.dlc_cycle_workspace_bytes(k, grouped, first), dlc.dlc_cycle_rda_workspace_bytes(k, grouped, first))
+            + 256) * 4
+
+    norms = {}  # sq_norms of each buffer set (RDA), by the codes buffer's address
 
     def buffers():
         codes, cb, rng = dlc.outputs_for(k, stride, len(grouped), DEV)
+        norms[codes.data_ptr()] = torch.zeros((k, len(grouped)), dtype=torch.float64, device=DEV)
         ws = torch.empty(need, dtype=torch.uint8, device=DEV)
         return codes, cb, rng, ws, inp.theta_g.clone(), inp.momentum.clone(), inp.theta_L.clone()
 
     codes_e, cb_e, rng_e, ws_e, th_e, mo_e, tl_e = buffers()
 
     def cycle(th, mo, tl, codes, cb, rng, ws, first_stream, others):
-        if n_lanes:
+        if rda:
+            dlc.dlc_outer_cycle_rda(th, mo, tl, grouped, first, weights, codes, cb, rng, norms[codes.data_ptr()], ws,
+                                    [first_stream] + others[:n_lanes - 1], broadcast=True)
+        elif n_lanes:
             dlc.dlc_outer_cycle_lanes(th, mo, tl, grouped, first, weights, codes, cb, rng, ws,
                                       [first_stream] + others[:n_lanes - 1], broadcast=True)
         else:
@@ -106,6 +115,8 @@ def test_captured_cycle_replays_the_eager_cycle(mode):
         torch.cuda.synchronize()
         assert torch.equal(th, th_e) and torch.equal(mo, mo_e) and torch.equal(tl, tl_e), rep
         assert torch.equal(cb, cb_e) and torch.equal(rng, rng_e), rep
+        if rda:
+            assert torch.equal(norms[codes.data_ptr()], norms[codes_e.data_ptr()]), rep
 
 
 @pytest.mark.parametrize("call", ["rda", "ring"])
@@ -128,6 +139,10 @@ def test_captured_rda_and_ring_replay_the_eager_calls(call):
             b["accum"], b["codes"], b["cb"], b["rng"] = dlc.ring_buffers(inp.theta_L, len(sizes))
             need = dlc.dlc_ring_workspace_bytes(k, inp.tensors)
         b["ws"] = torch.empty(max(256, need), dtype=torch.uint8, device=DEV)
+        # rows the call does not write (the ring writes one codebook and range row per
+        # non-empty chunk) must compare equal between the eager and the graph buffers
+        for key in ("codes", "cb", "rng"):
+            b[key].zero_()
         return b
 
     def run(b):
