@@ -291,9 +291,10 @@ def native_cycle(key, device, reps=5, warmup=2):
     stream, on two overlapped streams, on two streams with the update sent back to
     the learners (dlc_broadcast after each merge), with consecutive fragments on
     alternating lanes (DLC_TWO_LANES), on three and four lanes (dlc_outer_cycle_lanes),
-    and the three- and four-lane cycles captured in a HIP graph and replayed.  Four
-    lanes match the four hardware queues a process gets here; more lanes share them
-    and measured slower."""
+    and the three- and four-lane cycles captured in a HIP graph and replayed; then the
+    cycle merged by Radial-Directional Averaging (dlc_outer_cycle_rda) on one and four
+    lanes and from a graph.  Four lanes match the four hardware queues a process gets
+    here; more lanes share them and measured slower."""
     import statistics
     import torch
     import diloco_outer_step_amd as dlc
@@ -368,6 +369,48 @@ def native_cycle(key, device, reps=5, warmup=2):
             cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3), hbm_gbps=b / (ms_ * 1e-3) / 1e9,
             bytes_per_param=b // n_params)
         del graph
+
+    def timed(run):
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(qs)
+            run()
+            e1.record(qs)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return statistics.median(ts)
+
+    # every fragment merged by Radial-Directional Averaging (dlc_outer_cycle_rda;
+    # 24 + 11K bytes per parameter: one more read of the codes for the direction
+    # norm): one lane, four lanes, and four lanes replayed from a HIP graph
+    norms = torch.zeros((k, len(grouped)), dtype=torch.float64, device=device)
+    ws_rda = torch.empty(4 * (dlc.dlc_cycle_rda_workspace_bytes(k, grouped, first) + 256), dtype=torch.uint8,
+                         device=device)
+    b = (24 + 11 * k) * n_params
+
+    def rda(streams):
+        dlc.dlc_outer_cycle_rda(theta, mom, inp.theta_L, grouped, first, weights, codes, cb, rng, norms, ws_rda,
+                                streams)
+
+    def entry(ms_):
+        return dict(cycle_ms=ms_, params_per_s=n_params / (ms_ * 1e-3), hbm_gbps=b / (ms_ * 1e-3) / 1e9,
+                    bytes_per_param=b // n_params)
+
+    out["rda_one_lane"] = entry(timed(lambda: rda(lane_streams[:1])))
+    out["rda_four_lanes"] = entry(timed(lambda: rda(lane_streams)))
+    graph, side = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    others = [torch.cuda.Stream() for _ in range(3)]
+    side.wait_stream(qs)
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            rda([side] + others)
+    qs.wait_stream(side)
+    out["rda_four_lanes_graph"] = entry(timed(graph.replay))
+    del graph
     out["workload"] = cfg.title
     out["fragments"] = cfg.n_fragments
     return out
