@@ -10,7 +10,8 @@ through the C ABI and is compared with the oracle at the parity bar of
 tests/parity.py: end to end, and given the oracle's ranges (codes bit-exact).
 Half of the sets also run Radial-Directional Averaging (the bar of
 tests/test_gpu_rda.py); a third of them whole fragment cycles on one to four
-lanes, with and without sending the update back, against fragment-by-fragment
+lanes, with and without sending the update back, merged by the weighted mean and
+(every other set) by Radial-Directional Averaging, against fragment-by-fragment
 calls (bit-identical, as in tests/test_gpu_cycle.py); a third of them learners
 on one to three older bases (dlc_quantize_bases, the parity bar above); and the
 sets whose learners are all present the requantizing ring (the per-chunk checks
@@ -25,7 +26,7 @@ import diloco_outer_step_amd as dlc
 import oracle
 import workloads
 from tests import parity
-from tests.test_gpu_cycle import assert_same, run_cycle, run_sequential
+from tests.test_gpu_cycle import assert_same, run_cycle, run_cycle_rda, run_sequential, run_sequential_rda
 from tests.test_gpu_rda import check_merge_on_gpu_codes, gpu_rda
 from tests.test_gpu_ring import check_against_oracle, check_divergence_origins, gpu_ring
 
@@ -114,6 +115,14 @@ def test_random_set_cycle(seed):
     a = run_cycle(*args, broadcast=broadcast, two_streams=False, lanes=lanes)
     b = run_sequential(*args, broadcast=broadcast)
     assert_same(a, b, weights, grouped, first)
+    if seed % 2 == 0:  # the same cycle merged by Radial-Directional Averaging
+        a = run_cycle_rda(*args, broadcast=broadcast, lanes=lanes)
+        b = run_sequential_rda(*args, broadcast=broadcast)
+        assert_same(a, b, weights, grouped, first)
+        for f in range(n_fragments):
+            for i, w in enumerate(weights[f]):
+                if w > 0:
+                    assert torch.equal(a["sq_norms"][i, first[f]:first[f + 1]], b["sq_norms"][i, first[f]:first[f + 1]])
 
 
 @pytest.mark.parametrize("seed", SEEDS[1::3])
