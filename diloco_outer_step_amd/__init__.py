@@ -87,8 +87,8 @@ def _load() -> ctypes.CDLL:
         "dlc_ring_outer_step": [vp, vp, vp, i64, i32, tp, i32, ctypes.c_double, ctypes.c_double, vp, vp, vp, vp,
                                 vp, sz, vp],
         "dlc_rda_workspace_bytes": [i32, tp, i32, ctypes.POINTER(sz)],
-        "dlc_rda_outer_step": [vp, vp, vp, i64, i32, tp, i32, vp, ctypes.c_double, ctypes.c_double, vp, vp, vp, vp,
-                               vp, sz, vp],
+        "dlc_rda_outer_step": [vp, vp, vp, vp, i64, i32, tp, i32, vp, ctypes.c_double, ctypes.c_double, vp, vp, vp,
+                               vp, vp, sz, vp],
         "dlc_cycle_workspace_bytes": [i32, tp, vp, i32, ctypes.POINTER(sz)],
         "dlc_outer_cycle": [vp, vp, vp, i64, i32, vp, tp, vp, i32, vp, vp, vp, ctypes.c_double, ctypes.c_double,
                             u32, vp, sz, vp, vp],
@@ -427,18 +427,27 @@ def dlc_rda_workspace_bytes(n_learners: int, tensors) -> int:
 
 
 def dlc_rda_outer_step(theta_g, momentum, theta_L, tensors, weights, codes, codebook, range_out, sq_norms, workspace,
-                       lr=0.7, beta=0.9, stream=None):
+                       lr=0.7, beta=0.9, stream=None, bases=None):
     """One outer step merged by Radial-Directional Averaging; sq_norms is a device
-    fp64 [K, n_tensors] output (squared norms of the dequantized pseudo-gradients)."""
+    fp64 [K, n_tensors] output (squared norms of the dequantized pseudo-gradients).
+    bases: None (every learner against theta_g) or one device tensor per learner,
+    laid out like theta_g, that learner's pseudo-gradient is taken against."""
     c = _Checks()
     k, stride = c.learners(theta_L, tensors)
     w = _weights(weights, k)
     c.global_(tensors, theta_g=theta_g, momentum=momentum)
+    ptrs = None
+    if bases is not None:
+        if len(bases) != k:
+            raise ValueError("one base per learner")
+        c.global_(tensors, **{f"bases[{i}]": b for i, b in enumerate(bases) if weights[i] > 0})
+        ptrs = (ctypes.c_void_p * k)(*[b.data_ptr() for b in bases])
     c.outputs(k, len(tensors), codes, stride, codebook, range_out, sq_norms)
     c.workspace(workspace)
     c.done()
     arr, n = _tensors(tensors)
-    _check(_lib.dlc_rda_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L), stride, k, arr, n,
+    _check(_lib.dlc_rda_outer_step(_ptr(theta_g), _ptr(momentum), _ptr(theta_L),
+                                   None if ptrs is None else ctypes.cast(ptrs, ctypes.c_void_p), stride, k, arr, n,
                                    ctypes.cast(w, ctypes.c_void_p), float(lr), float(beta), _ptr(codes),
                                    _ptr(codebook), _ptr(range_out), _ptr(sq_norms), _ptr(workspace),
                                    workspace.numel(), _stream(stream)))

@@ -656,6 +656,32 @@ size_t quantize_workspace(const dlc_tensor* tensors, int32_t n_tensors, int32_t 
   return workspace_layout(ps.n_slots, pe.n_slots, n_tensors, kp).total;
 }
 
+// Learners grouped by base (groups in order of first appearance), one quantize
+// setup per group on the same workspace (the groups run one after another on the
+// stream); every group checked before anything is enqueued.
+int32_t setup_base_groups(std::vector<Common>& groups, const float* const* bases, const float* theta_learners,
+                          int64_t learner_stride, int32_t n_learners, const uint8_t* present,
+                          const dlc_tensor* tensors, int32_t n_tensors, void* workspace, size_t workspace_bytes,
+                          void* hip_stream) {
+  std::vector<const float*> order;
+  for (int32_t i = 0; i < n_learners; ++i) {
+    if (present != nullptr && present[i] == 0) continue;
+    if (!bases[i]) return fail(DLC_ERR_INVALID_ARGUMENT, "bases[" + std::to_string(i) + "] is NULL");
+    if (std::find(order.begin(), order.end(), bases[i]) == order.end()) order.push_back(bases[i]);
+  }
+  if (order.empty()) return fail(DLC_ERR_NO_QUORUM, "no learner is present");
+  groups.assign(order.size(), Common());
+  std::vector<uint8_t> member(n_learners);
+  for (size_t gi = 0; gi < order.size(); ++gi) {
+    for (int32_t i = 0; i < n_learners; ++i)
+      member[i] = (present == nullptr || present[i] != 0) && bases[i] == order[gi] ? 1 : 0;
+    const int32_t rc = setup_quant(groups[gi], order[gi], theta_learners, learner_stride, n_learners, member.data(),
+                                   tensors, n_tensors, workspace, workspace_bytes, hip_stream);
+    if (rc != DLC_OK) return rc;
+  }
+  return DLC_OK;
+}
+
 // The static scratch of dlc_quantize_static (the array is declared at the top of
 // this file).  Host code never uses the array's name as an address: its address
 // on each device comes from hipGetSymbolAddress, looked up once per device (the
@@ -823,26 +849,14 @@ int32_t dlc_quantize_bases(const float* const* bases, const float* theta_learner
   if (!range || !codes || !codebook) return fail(DLC_ERR_INVALID_ARGUMENT, "range, codes and codebook must not be NULL");
   if (!aligned256(range) || !aligned256(codes) || !aligned256(codebook))
     return fail(DLC_ERR_ALIGNMENT, "range, codes and codebook must be 256-byte aligned");
-  // learners grouped by base, groups in order of first appearance; every group
-  // checked before anything is enqueued
-  std::vector<const float*> order;
-  for (int32_t i = 0; i < n_learners; ++i) {
-    if (present != nullptr && present[i] == 0) continue;
-    if (!bases[i]) return fail(DLC_ERR_INVALID_ARGUMENT, "bases[" + std::to_string(i) + "] is NULL");
-    if (std::find(order.begin(), order.end(), bases[i]) == order.end()) order.push_back(bases[i]);
-  }
-  if (order.empty()) return fail(DLC_ERR_NO_QUORUM, "no learner is present");
-  std::vector<Common> groups(order.size());
-  std::vector<uint8_t> member(n_learners);
-  for (size_t gi = 0; gi < order.size(); ++gi) {
-    for (int32_t i = 0; i < n_learners; ++i)
-      member[i] = (present == nullptr || present[i] != 0) && bases[i] == order[gi] ? 1 : 0;
-    int32_t rc = setup_quant(groups[gi], order[gi], theta_learners, learner_stride, n_learners, member.data(), tensors,
-                             n_tensors, workspace, workspace_bytes, hip_stream);
-    if (rc != DLC_OK) return rc;
-    groups[gi].args.range = reinterpret_cast<float4*>(range);
-    groups[gi].args.codes = codes;
-    groups[gi].args.codebook = codebook;
+  std::vector<Common> groups;
+  int32_t rc = setup_base_groups(groups, bases, theta_learners, learner_stride, n_learners, present, tensors,
+                                 n_tensors, workspace, workspace_bytes, hip_stream);
+  if (rc != DLC_OK) return rc;
+  for (Common& c : groups) {
+    c.args.range = reinterpret_cast<float4*>(range);
+    c.args.codes = codes;
+    c.args.codebook = codebook;
   }
   // one workspace: the groups run one after another on the stream
   for (Common& c : groups) {
@@ -1113,7 +1127,8 @@ int32_t dlc_rda_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, i
 }
 
 int32_t dlc_rda_outer_step(float* theta_global, float* momentum, const float* theta_learners,
-                           int64_t learner_stride, int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                           const float* const* bases, int64_t learner_stride, int32_t n_learners,
+                           const dlc_tensor* tensors, int32_t n_tensors,
                            const double* weights, double lr, double beta, uint8_t* codes, float* codebook,
                            float* range, double* sq_norms, void* workspace, size_t workspace_bytes,
                            void* hip_stream) {
@@ -1128,27 +1143,38 @@ int32_t dlc_rda_outer_step(float* theta_global, float* momentum, const float* th
   const RdaWorkspace rw = rda_workspace(n_learners, tensors, n_tensors);
   if (workspace == nullptr || workspace_bytes < rw.total)
     return fail(DLC_ERR_WORKSPACE, "workspace too small: need " + std::to_string(rw.total) + " bytes");
-  // learners with a positive weight are quantized and merged
+  // learners with a positive weight are quantized and merged, against theta_global
+  // or, with bases, each against its own base (one quantize per distinct base)
   std::vector<uint8_t> present(n_learners);
   for (int32_t i = 0; i < n_learners; ++i) present[i] = weights[i] > 0.0 ? 1 : 0;
-  Common c;
-  rc = setup_quant(c, theta_global, theta_learners, learner_stride, n_learners, present.data(), tensors, n_tensors,
-                   workspace, rw.quant, hip_stream);
+  std::vector<Common> groups;
+  if (bases == nullptr) {
+    groups.resize(1);
+    rc = setup_quant(groups[0], theta_global, theta_learners, learner_stride, n_learners, present.data(), tensors,
+                     n_tensors, workspace, rw.quant, hip_stream);
+  } else {
+    rc = setup_base_groups(groups, bases, theta_learners, learner_stride, n_learners, present.data(), tensors,
+                           n_tensors, workspace, rw.quant, hip_stream);
+  }
   if (rc != DLC_OK) return rc;
-  c.args.range = reinterpret_cast<float4*>(range);
-  c.args.codes = codes;
-  c.args.codebook = codebook;
-  c.args.norm2 = sq_norms;
+  for (Common& c : groups) {
+    c.args.range = reinterpret_cast<float4*>(range);
+    c.args.codes = codes;
+    c.args.codebook = codebook;
+    c.args.norm2 = sq_norms;
+  }
   char* ws = static_cast<char*>(workspace);
   ma.norm2 = sq_norms;
   ma.dir_part = reinterpret_cast<double*>(ws + rw.dir_part);
   ma.coef = nullptr;
   double* coef = reinterpret_cast<double*>(ws + rw.coef);
   const Partition pm = direction_partition(tensors, n_tensors);
-  rc = run_range(c);
-  if (rc == DLC_OK) rc = run_encode(c);
-  if (rc != DLC_OK) return rc;
-  const hipStream_t st = c.stream;
+  for (Common& c : groups) {
+    rc = run_range(c);
+    if (rc == DLC_OK) rc = run_encode(c);
+    if (rc != DLC_OK) return rc;
+  }
+  const hipStream_t st = groups[0].stream;
   for (const dlc::LaunchGeom& g : pm.launches) {
     hipError_t e = dlc::launch_rda_direction(ma, g, st);
     if (e != hipSuccess) return hip_fail(e, "direction kernel launch");

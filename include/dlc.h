@@ -428,6 +428,12 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
  * Learners with weight 0 are absent: neither quantized nor read, and their rows
  * of every output are left untouched.  Results agree with the fp64 definition up
  * to the order of fp64 rounding (not bit for bit).
+ *   bases     NULL: every pseudo-gradient is fl32(theta_global - theta_i); or a
+ *             host array [n_learners] of device pointers, each laid out like
+ *             theta_global: learner i's pseudo-gradient is fl32(bases[i] -
+ *             theta_i), the version it started from (as dlc_quantize_bases; the
+ *             Decoupled DiLoCo digest's asynchronous learners, merged by its
+ *             syncer's rule); theta_global is still the state the step updates
  *   codes     device uint8 [n_learners][learner_stride], written (as dlc_quantize)
  *   codebook  device fp32 [n_learners][n_tensors][256], written
  *   range     device fp32 [n_learners][n_tensors][4], written
@@ -440,7 +446,8 @@ int32_t dlc_ring_outer_step(float* theta_global, float* momentum, const float* t
 int32_t dlc_rda_workspace_bytes(int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors, size_t* bytes);
 
 int32_t dlc_rda_outer_step(float* theta_global, float* momentum, const float* theta_learners,
-                           int64_t learner_stride, int32_t n_learners, const dlc_tensor* tensors, int32_t n_tensors,
+                           const float* const* bases, int64_t learner_stride, int32_t n_learners,
+                           const dlc_tensor* tensors, int32_t n_tensors,
                            const double* weights, double lr, double beta, uint8_t* codes, float* codebook,
                            float* range, double* sq_norms, void* workspace, size_t workspace_bytes,
                            void* hip_stream);

@@ -167,10 +167,10 @@ int main(void) {
                             NULL) == DLC_ERR_INVALID_ARGUMENT,
         "ring: infinite lr rejected");
   const double zeros4[4] = {0.0, 0.0, 0.0, 0.0};
-  check(dlc_rda_outer_step(F, F, F, 1 << 20, 4, ragged, 5, zeros4, 0.7, 0.9, U, F, F, (double*)F, W,
+  check(dlc_rda_outer_step(F, F, F, NULL, 1 << 20, 4, ragged, 5, zeros4, 0.7, 0.9, U, F, F, (double*)F, W,
                            (size_t)1 << 40, NULL) == DLC_ERR_NO_QUORUM,
         "RDA: all-zero weights are a failed quorum");
-  check(dlc_rda_outer_step(F, F, F, 1 << 20, 4, ragged, 5, ones, 0.7, 0.9, U, F, F, (double*)F, W, 256, NULL) ==
+  check(dlc_rda_outer_step(F, F, F, NULL, 1 << 20, 4, ragged, 5, ones, 0.7, 0.9, U, F, F, (double*)F, W, 256, NULL) ==
             DLC_ERR_WORKSPACE,
         "RDA: small workspace rejected");
   check(dlc_merge_weights(4, tokens, arrival, 4, 0.5, w, &when) == DLC_ERR_NO_QUORUM,

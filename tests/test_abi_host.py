@@ -198,8 +198,8 @@ def ring(k=2, spec=((0, 0, 4096),), stride=4096, lr=0.7, ws_bytes=16, accum=FAKE
 def rda(k=2, spec=((0, 0, 4096),), stride=4096, weights=(1.0, 1.0), norms=FAKE, ws_bytes=16, theta=FAKE):
     arr, n = tens(spec)
     w = (ctypes.c_double * k)(*weights)
-    return L.dlc_rda_outer_step(theta, FAKE, FAKE, stride, k, arr, n, ctypes.cast(w, ctypes.c_void_p), 0.7, 0.9,
-                                FAKE, FAKE, FAKE, norms, FAKE, ws_bytes, None)
+    return L.dlc_rda_outer_step(theta, FAKE, FAKE, None, stride, k, arr, n, ctypes.cast(w, ctypes.c_void_p), 0.7,
+                                0.9, FAKE, FAKE, FAKE, norms, FAKE, ws_bytes, None)
 
 
 @pytest.mark.parametrize("call,code", [

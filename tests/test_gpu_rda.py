@@ -11,7 +11,9 @@
   all match is within the theta/momentum tolerance of tests/parity.py;
 * degenerate cases: learners that did not move (zero norms: a pure momentum
   step), zero-variance tensors, absent learners, one learner (the star step),
-  more than 16 learners (the run-time learner loop), a full-size parameter set.
+  more than 16 learners (the run-time learner loop), a full-size parameter set;
+* learners on older bases (one call with bases) against the oracle's step with
+  the same bases, and theta_global passed as every base equal to no bases.
 """
 import numpy as np
 import pytest
@@ -22,6 +24,7 @@ import oracle
 import workloads
 from tests import parity
 from tests.test_gpu_parity import case_inputs
+from tests.test_gpu_stale import stale_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -184,6 +187,46 @@ def test_balanced_constant_learners_cancel():
     th_o, mo_o = oracle.nesterov(theta0[off:off + n], mom0[off:off + n], np.zeros(n), LR, BETA)
     assert np.array_equal(parity.host(gpu["momentum"])[off:off + n], mo_o)
     assert np.array_equal(parity.host(gpu["theta"])[off:off + n], th_o)
+
+
+def test_stale_bases_rda_against_oracle():
+    """Learners that started from three versions of the global parameters (the
+    digest's asynchronous learners), token weights, one learner absent, merged by
+    Radial-Directional Averaging in one call: the quantization at the parity bar
+    against the oracle's with the same bases, and the oracle's RDA merge and
+    Nesterov step on the GPU's own codes within one ulp."""
+    theta, mom, theta_L, tensors, bases = stale_inputs(5)
+    k, stride = theta_L.shape
+    weights = [4096.0 * (i + 1) for i in range(k)]
+    weights[2] = 0.0
+    present = [1 if w > 0 else 0 for w in weights]
+    codes, cb, rng, norms, ws = rda_buffers(k, stride, len(tensors), tensors)
+    th, mo = theta.clone(), mom.clone()
+    dlc.dlc_rda_outer_step(th, mo, theta_L, tensors, weights, codes, cb, rng, norms, ws, LR, BETA, bases=bases)
+    torch.cuda.synchronize()
+    gpu = dict(codes=codes, codebook=cb, range=rng, sq_norms=norms, theta=th, momentum=mo)
+    theta0, mom0 = parity.host(theta), parity.host(mom)
+    orc = oracle.outer_step(theta0, mom0, parity.host(theta_L), stride, tensors, weights, present, LR, BETA,
+                            bases=[parity.host(b) for b in bases], rule="rda")
+    view = workloads.StepInputs(theta, mom, theta_L, tensors, weights, present, list(range(len(tensors))), stride)
+    parity.compare(gpu, orc, view, pinned=False, state=False)
+    check_merge_on_gpu_codes(gpu, view, theta0, mom0)
+
+
+def test_rda_with_theta_g_as_every_base_equals_no_bases():
+    inp = make_inputs(41, 5, SIZES, [1.0, 0.0, 2.0, 0.5, 1.5])
+    k = inp.theta_L.shape[0]
+    a = gpu_rda(inp)
+    codes, cb, rng, norms, ws = rda_buffers(k, inp.theta_L.shape[1], len(inp.tensors), inp.tensors)
+    th, mo = inp.theta_g.clone(), inp.momentum.clone()
+    dlc.dlc_rda_outer_step(th, mo, inp.theta_L, inp.tensors, inp.weights, codes, cb, rng, norms, ws, LR, BETA,
+                           bases=[inp.theta_g] * k)
+    torch.cuda.synchronize()
+    assert torch.equal(th, a["theta"]) and torch.equal(mo, a["momentum"])
+    for i in range(k):
+        if inp.weights[i] > 0:
+            assert torch.equal(cb[i], a["codebook"][i]) and torch.equal(rng[i], a["range"][i])
+            assert torch.equal(norms[i], a["sq_norms"][i])
 
 
 @pytest.mark.slow
