@@ -353,7 +353,7 @@ def dlc_merge_outer_step(theta_g, momentum, codes, codebook, weights, tensors, l
 def dlc_quantize_bases(bases, theta_L, tensors, codes, codebook, range_out, workspace, present=None,
                        stream=None):
     """dlc_quantize with learner i's pseudo-gradient taken against bases[i] (a
-    device tensor laid out like theta_g)."""
+    device tensor laid out like theta_g; None for a learner that is not present)."""
     c = _Checks()
     k, stride = c.learners(theta_L, tensors)
     if len(bases) != k:
@@ -365,7 +365,7 @@ def dlc_quantize_bases(bases, theta_L, tensors, codes, codebook, range_out, work
     c.done()
     arr, n = _tensors(tensors)
     _buf, pres = _present(present, k)
-    ptrs = (ctypes.c_void_p * k)(*[b.data_ptr() for b in bases])
+    ptrs = (ctypes.c_void_p * k)(*[0 if b is None else b.data_ptr() for b in bases])
     _check(_lib.dlc_quantize_bases(ctypes.cast(ptrs, ctypes.c_void_p), _ptr(theta_L), stride, k,
                                    pres, arr, n, _ptr(codes), _ptr(codebook), _ptr(range_out), _ptr(workspace),
                                    workspace.numel(), _stream(stream)))
@@ -431,7 +431,8 @@ def dlc_rda_outer_step(theta_g, momentum, theta_L, tensors, weights, codes, code
     """One outer step merged by Radial-Directional Averaging; sq_norms is a device
     fp64 [K, n_tensors] output (squared norms of the dequantized pseudo-gradients).
     bases: None (every learner against theta_g) or one device tensor per learner,
-    laid out like theta_g, that learner's pseudo-gradient is taken against."""
+    laid out like theta_g, that learner's pseudo-gradient is taken against (None
+    for a learner of weight 0)."""
     c = _Checks()
     k, stride = c.learners(theta_L, tensors)
     w = _weights(weights, k)
@@ -441,7 +442,7 @@ def dlc_rda_outer_step(theta_g, momentum, theta_L, tensors, weights, codes, code
         if len(bases) != k:
             raise ValueError("one base per learner")
         c.global_(tensors, **{f"bases[{i}]": b for i, b in enumerate(bases) if weights[i] > 0})
-        ptrs = (ctypes.c_void_p * k)(*[b.data_ptr() for b in bases])
+        ptrs = (ctypes.c_void_p * k)(*[0 if b is None else b.data_ptr() for b in bases])
     c.outputs(k, len(tensors), codes, stride, codebook, range_out, sq_norms)
     c.workspace(workspace)
     c.done()

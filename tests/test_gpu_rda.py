@@ -202,7 +202,9 @@ def test_stale_bases_rda_against_oracle():
     present = [1 if w > 0 else 0 for w in weights]
     codes, cb, rng, norms, ws = rda_buffers(k, stride, len(tensors), tensors)
     th, mo = theta.clone(), mom.clone()
-    dlc.dlc_rda_outer_step(th, mo, theta_L, tensors, weights, codes, cb, rng, norms, ws, LR, BETA, bases=bases)
+    passed = list(bases)
+    passed[2] = None  # the absent learner needs no base
+    dlc.dlc_rda_outer_step(th, mo, theta_L, tensors, weights, codes, cb, rng, norms, ws, LR, BETA, bases=passed)
     torch.cuda.synchronize()
     gpu = dict(codes=codes, codebook=cb, range=rng, sq_norms=norms, theta=th, momentum=mo)
     theta0, mom0 = parity.host(theta), parity.host(mom)
